@@ -1,0 +1,41 @@
+"""CPU fp64 oracle for exact attention (test infrastructure only).
+
+This package is the checker, not the product.  Only the test suite, the
+``smoke()`` entry of ``__graft_entry__`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it.  The GPU library never calls into it, and it
+shares no code with the GPU library: no kernels, no helpers, no constants.
+
+What it computes, and where that is defined:
+
+* Attention is the softmax of the scaled query-key products over the keys a
+  query may see, weighted over the value rows.  The tiled online-softmax
+  kernel of "Guia Prático de Programação de GPU com Tiles: de Kernels cuTile
+  e Triton ao Flash Attention" (Passo a Passo, step 6 "Flash Attention —
+  Softmax Online") reaches this same result block by block; the running
+  max / running sum recurrence there telescopes exactly to the full softmax,
+  so the oracle writes out the full softmax directly (fp64, explicit
+  max-subtraction as in step 4 "Softmax por Linha").
+* Grouped-query attention (query heads sharing a key/value head) is named
+  as a feature of the final kernel of "Como Domar o Blackwell Sem Enlouquecer
+  com CUDA" (section "O Que Tem Dentro Deste Tutorial").  Reading: query head
+  ``h`` uses key/value head ``h // (Hq // Hkv)``.
+* Causal masking is named as a feature of the production library in the FAQ
+  of the first page.  Reading: key ``j`` is visible to query ``i`` iff
+  ``j <= i`` (top-left aligned, also when ``Sq != Sk``).
+* The per-row log-sum-exp is not on the pages.  Reading: natural log of the
+  softmax denominator of the *scaled* scores, ``lse = m + ln(sum exp(s - m))``.
+
+Modules:
+
+* ``full_softmax`` — vectorised numpy fp64 definition (full and row-sampled).
+* ``brute``     — pure-Python triple loop with ``math.fsum``; tiny inputs only.
+
+Every function here is pinned by ``-m "not gpu"`` tests against facts that
+do not come from the oracle itself (closed forms, invariants, a library
+routine, brute force); see ``tests/test_oracle_pins.py``.
+"""
+
+from .full_softmax import attention, attention_rows, visible_count
+from .brute import attention_bruteforce
+
+__all__ = ["attention", "attention_rows", "visible_count", "attention_bruteforce"]

@@ -1,0 +1,17 @@
+"""Shared pytest configuration.
+
+Tests marked ``gpu`` need an MI355X (gfx950) and the built HIP library; the
+rest run on any CPU.  ``python -m pytest -m "not gpu"`` is the CPU suite.
+"""
+
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: long-running (full-size workloads)")

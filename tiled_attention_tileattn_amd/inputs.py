@@ -1,0 +1,105 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle checks.
+
+This module draws random numbers and nothing else: it holds none of the
+attention arithmetic, so both the GPU path and the CPU oracle can be fed from
+it without sharing any of the method's code.
+
+Recipe (the same for every workload):
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = randn([B, Hq,  Sq, D]) * q_std      (float32, drawn first)
+    k = randn([B, Hkv, Sk, D]) * k_std      (drawn second)
+    v = randn([B, Hkv, Sk, D]) * v_std      (drawn third)
+    then cast to the workload dtype (bfloat16 casts round to nearest even).
+A row sample for the long-context workload continues the same generator
+after v: randperm(B * Hq * Sq)[:n], flat indices into [B, Hq, Sq].
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Sk: int
+    D: int
+    causal: bool
+    dtype: str          # "bf16" or "fp32"
+    seed: int
+    q_std: float = 1.0
+    k_std: float = 1.0
+    v_std: float = 1.0
+    sample_rows: int = 0   # >0: the oracle is checked on this many sampled rows
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(D), as the float32 value the GPU receives."""
+        return float(np.float32(1.0 / math.sqrt(self.D)))
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def flop(self) -> float:
+        """Counted attention FLOP: 4*B*Hq*Sq*Sk*D, halved when causal."""
+        f = 4.0 * self.B * self.Hq * self.Sq * self.Sk * self.D
+        return f / 2 if self.causal else f
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five workloads: a tiny fp32 case, plain multi-head bf16, causal multi-head,
+# causal grouped-query at 8K (the headline), and long-context grouped-query at 32K.
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", 1, 1, 1, 128, 128, 64, False, "fp32", 0),
+    "mha_bf16": Workload("mha_bf16", 4, 8, 8, 1024, 1024, 64, False, "bf16", 1),
+    "causal_mha_bf16": Workload("causal_mha_bf16", 2, 16, 16, 4096, 4096, 128, True, "bf16", 2),
+    "causal_gqa_bf16": Workload("causal_gqa_bf16", 1, 32, 8, 8192, 8192, 128, True, "bf16", 3),
+    "longctx_gqa_bf16": Workload("longctx_gqa_bf16", 1, 64, 8, 32768, 32768, 128, True, "bf16", 4,
+                                 q_std=0.5, k_std=0.5, sample_rows=256),
+}
+
+HEADLINE = "causal_gqa_bf16"
+
+
+def make_inputs(w: Workload, device: str | torch.device = "cpu", with_sample: bool = False):
+    """Draw (q, k, v[, sample]) for workload ``w`` following the module recipe.
+
+    The draw always happens on the CPU generator, so the values do not depend
+    on ``device``; the tensors are then moved there.
+    """
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    q = torch.randn((w.B, w.Hq, w.Sq, w.D), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.Hkv, w.Sk, w.D), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.Hkv, w.Sk, w.D), generator=g, dtype=torch.float32)
+    if w.q_std != 1.0:
+        q.mul_(w.q_std)
+    if w.k_std != 1.0:
+        k.mul_(w.k_std)
+    if w.v_std != 1.0:
+        v.mul_(w.v_std)
+    dt = w.torch_dtype
+    q, k, v = (t.to(dt).contiguous().to(device) for t in (q, k, v))
+    if not with_sample:
+        return q, k, v
+    n = w.sample_rows if w.sample_rows > 0 else 256
+    total = w.B * w.Hq * w.Sq
+    sample = torch.randperm(total, generator=g)[: min(n, total)].numpy()
+    return q, k, v, sample
+
+
+def random_qkv(B, Hq, Hkv, Sq, Sk, D, dtype="bf16", seed=0, q_std=1.0, k_std=1.0, v_std=1.0,
+               device="cpu"):
+    """Ad-hoc shapes for tests, same recipe as ``make_inputs``."""
+    w = Workload("adhoc", B, Hq, Hkv, Sq, Sk, D, False, dtype, seed, q_std, k_std, v_std)
+    return make_inputs(w, device=device)
