@@ -1,0 +1,103 @@
+/*
+ * tileattn — exact attention forward for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * Computes, for every batch b, query head h and query row i,
+ *
+ *     s_ij   = scale * <q[b,h,i,:], k[b,hk,j,:]>          for visible keys j
+ *     o[b,h,i,:] = sum_j softmax_j(s_i) * v[b,hk,j,:]
+ *     lse[b,h,i] = ln( sum_j exp(s_ij) )                  (natural log)
+ *
+ * tile by tile with an online (running max / running sum) softmax, so the
+ * Sq x Sk score matrix never exists in memory.  That method is the flash
+ * attention kernel of "Guia Prático de Programação de GPU com Tiles: de
+ * Kernels cuTile e Triton ao Flash Attention" (Passo a Passo, step 6
+ * "Flash Attention — Softmax Online"): a query tile stays resident while key
+ * and value tiles stream past it; per tile the scores are formed, the running
+ * row maximum is raised, the running sum and the accumulator are rescaled by
+ * exp(old max - new max), and probabilities (cast to the value dtype) are
+ * multiplied into the accumulator, which is divided by the running sum at the
+ * end.  Products accumulate in fp32 (step 5 "Multiplicação de Matrizes Tiled"
+ * and its Troubleshooting note on fp16 accumulators).
+ *
+ * Readings of what the pages leave open:
+ *   - GQA (named for the final kernel of "Como Domar o Blackwell Sem
+ *     Enlouquecer com CUDA", section "O Que Tem Dentro Deste Tutorial"):
+ *     query head h reads key/value head hk = h / (Hq / Hkv).
+ *   - causal (named in the FAQ of the first page as a production feature):
+ *     key j is visible to query i iff j <= i, top-left aligned for any Sq, Sk.
+ *   - lse is not on the pages: natural log of the softmax denominator of the
+ *     scaled scores, stored as fp32.
+ *
+ * Layout: every tensor is dense row-major with the head dimension innermost:
+ *     q   [B, Hq,  Sq, D]      k, v [B, Hkv, Sk, D]
+ *     o   [B, Hq,  Sq, D]      lse  [B, Hq,  Sq]      (fp32)
+ * All pointers are device pointers on the current HIP device, 16-byte
+ * aligned.  The caller owns every buffer; the library allocates nothing,
+ * keeps no state between calls and is safe to call from several host
+ * threads.  o and lse must not overlap q, k or v.
+ *
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ * stream).  Argument errors are reported before anything is launched; a
+ * launch failure is reported as TILEATTN_ERR_LAUNCH; faults inside the kernel
+ * surface at the caller's next synchronisation with the stream.
+ */
+#ifndef TILEATTN_H
+#define TILEATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TILEATTN_OK = 0,
+  TILEATTN_ERR_NULL_POINTER = -1, /* q, k, v, o or lse is NULL (non-empty problem)   */
+  TILEATTN_ERR_BAD_SHAPE = -2,    /* a size < 0, or Hkv < 1 or Sk < 1                 */
+  TILEATTN_ERR_GQA_RATIO = -3,    /* Hq is not a multiple of Hkv                      */
+  TILEATTN_ERR_HEAD_DIM = -4,     /* D is not 64 or 128                               */
+  TILEATTN_ERR_SCALE = -5,        /* scale is negative, NaN or infinite               */
+  TILEATTN_ERR_ALIGNMENT = -6,    /* a pointer is not 16-byte aligned                 */
+  TILEATTN_ERR_TOO_LARGE = -7,    /* a size product exceeds the 64-bit index range    */
+  TILEATTN_ERR_LAUNCH = -8        /* the HIP launch failed (e.g. no gfx950 device)    */
+} tileattn_status;
+
+/*
+ * bfloat16 attention forward (the hot path).
+ *   q, k, v : bf16 inputs, layouts above.
+ *   o       : bf16 output [B, Hq, Sq, D], rounded to nearest even from fp32.
+ *   lse     : fp32 output [B, Hq, Sq].
+ *   B, Hq, Sq may be 0 (nothing is launched, TILEATTN_OK).  Hkv >= 1, Sk >= 1.
+ *   D in {64, 128}.  scale >= 0 and finite (usually 1/sqrt(D)).
+ *   causal != 0 applies the top-left causal mask (key j visible iff j <= i).
+ *   stream  : hipStream_t to launch on, NULL for the default stream.
+ * Returns TILEATTN_OK or a tileattn_status error code.
+ */
+int tileattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                 float scale, int causal, void* stream);
+
+/*
+ * float32 attention forward: the same contract as tileattn_fwd with fp32
+ * q, k, v and o.  Both products use fp32 matrix-core instructions and the
+ * probabilities stay fp32 (there is no narrower value dtype to cast them to).
+ */
+int tileattn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                     float scale, int causal, void* stream);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* tileattn_strerror(int status);
+
+/*
+ * Launch geometry the library uses for a problem: query rows per workgroup
+ * (block_m), keys per tile (block_n) and the number of workgroups.  For
+ * reporting and tests; pure host arithmetic, no HIP call.  dtype_bytes is 2
+ * (bf16) or 4 (fp32).  Returns TILEATTN_OK or the error tileattn_fwd would.
+ */
+int tileattn_launch_shape(int dtype_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                          int causal, int* block_m, int* block_n, long long* workgroups);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILEATTN_H */

@@ -1,0 +1,238 @@
+"""Parity of the HIP kernels with the CPU fp64 oracle (needs an MI355X).
+
+Every comparison calls the library through the C ABI (the ctypes binding)
+on seeded inputs from ``tiled_attention_tileattn_amd.inputs`` and compares
+element by element with ``oracle`` on the same input values.
+
+Tolerances (on O, over all compared elements):
+    bf16 inputs: max |err| <= 2e-2 and mean |err| <= 2e-3
+    fp32 inputs: max |err| <= 1e-4
+On lse (not specified elsewhere; derived from the arithmetic: fp32 sums of
+exact products and the hardware exp2/log): <= 1e-3 (bf16), <= 1e-4 (fp32).
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_attention_tileattn_amd as ta
+from tiled_attention_tileattn_amd.inputs import WORKLOADS, make_inputs, random_qkv
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": dict(max=2e-2, mean=2e-3, lse=1e-3), "fp32": dict(max=1e-4, mean=1e-4, lse=1e-4)}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    ta.load_library()
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _gpu_forward(q, k, v, causal, scale):
+    qd, kd, vd = (t.to("cuda") for t in (q, k, v))
+    o, lse = ta.forward(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _errs(o_gpu, o_ref):
+    err = np.abs(o_gpu.astype(np.float64) - o_ref)
+    return float(err.max()), float(err.mean())
+
+
+def _check(o, lse, o_ref, lse_ref, dtype, what=""):
+    tol = TOL[dtype]
+    o = o.detach().to("cpu", torch.float64).numpy()
+    lse = lse.detach().to("cpu", torch.float64).numpy()
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    mx, mean = _errs(o, o_ref)
+    lmx = float(np.abs(lse - lse_ref).max()) if lse.size else 0.0
+    _say(f"  {what}: max|dO|={mx:.3e} mean|dO|={mean:.3e} max|dlse|={lmx:.3e}")
+    assert mx <= tol["max"], f"{what}: max abs err {mx}"
+    assert mean <= tol["mean"], f"{what}: mean abs err {mean}"
+    assert lmx <= tol["lse"], f"{what}: lse err {lmx}"
+
+
+def _parity(B, Hq, Hkv, Sq, Sk, D, causal, dtype, seed, scale=None, q_std=1.0, k_std=1.0):
+    scale = float(np.float32(1.0 / math.sqrt(D))) if scale is None else scale
+    what = f"B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} D={D} causal={causal} {dtype} seed={seed}"
+    _say(what)
+    q, k, v = random_qkv(B, Hq, Hkv, Sq, Sk, D, dtype=dtype, seed=seed, q_std=q_std, k_std=k_std)
+    o, lse = _gpu_forward(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal)
+    _check(o, lse, o_ref, lse_ref, dtype, what)
+    return q, k, v, o, lse
+
+
+# ---------------------------------------------------------------------------
+# Small sweep: tails around the 128-row / 64-key tiles, Sq != Sk, GQA ratios.
+# ---------------------------------------------------------------------------
+SWEEP = [
+    # B, Hq, Hkv, Sq, Sk, D
+    (1, 1, 1, 1, 1, 64), (1, 2, 1, 2, 2, 128), (1, 4, 2, 7, 13, 64), (2, 2, 2, 13, 7, 128),
+    (1, 8, 1, 16, 16, 128), (1, 2, 2, 17, 17, 64), (1, 4, 1, 64, 64, 128), (1, 2, 1, 127, 129, 128),
+    (2, 4, 4, 128, 128, 64), (1, 8, 2, 129, 127, 128), (1, 4, 2, 300, 300, 128),
+    (1, 2, 2, 300, 65, 64), (1, 2, 1, 63, 300, 128), (1, 16, 2, 257, 257, 128),
+    (1, 1, 1, 1, 300, 128), (1, 1, 1, 300, 1, 64),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SWEEP)
+def test_sweep_bf16(shape, causal):
+    _parity(*shape, causal=causal, dtype="bf16", seed=sum(shape))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SWEEP[::2])
+def test_sweep_fp32(shape, causal):
+    _parity(*shape, causal=causal, dtype="fp32", seed=7 + sum(shape))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_scale_edge_values(dtype):
+    # scale = 0: every visible key weighs the same; large scale: peaky softmax.
+    _parity(1, 4, 2, 150, 150, 128, True, dtype, seed=3, scale=0.0)
+    _parity(1, 4, 2, 150, 150, 64, False, dtype, seed=4, scale=1.0)
+    _parity(1, 2, 1, 200, 200, 128, True, dtype, seed=5, q_std=4.0, k_std=4.0)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and invariants on the kernel's outputs.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_key_returns_value_row(causal):
+    q, k, v = random_qkv(2, 8, 2, 200, 1, 128, dtype="bf16", seed=11)
+    o, lse = _gpu_forward(q, k, v, causal, 0.0883883461356163)
+    expect = v.repeat_interleave(4, dim=1).expand(2, 8, 200, 128)
+    assert torch.equal(o.cpu(), expect), "Sk=1 must return v[0] exactly"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_returns_mean_of_visible_values(causal):
+    B, Hq, Hkv, S, D = 1, 4, 2, 333, 128
+    _, k, v = random_qkv(B, Hq, Hkv, S, S, D, dtype="bf16", seed=12)
+    q = torch.zeros(B, Hq, S, D, dtype=torch.bfloat16)
+    o, lse = _gpu_forward(q, k, v, causal, 0.0883883461356163)
+    vd = v.double().repeat_interleave(2, dim=1)
+    if causal:
+        mean = vd.cumsum(2) / torch.arange(1, S + 1, dtype=torch.float64)[None, None, :, None]
+        lse_ref = torch.log(torch.arange(1, S + 1, dtype=torch.float64)).expand(B, Hq, S)
+    else:
+        mean = vd.mean(2, keepdim=True).expand(B, Hq, S, D)
+        lse_ref = torch.full((B, Hq, S), math.log(S), dtype=torch.float64)
+    _check(o, lse, mean.numpy(), lse_ref.numpy(), "bf16", f"zero query causal={causal}")
+
+
+@pytest.mark.parametrize("c", [0.75, -1.5])
+def test_constant_values_return_the_constant(c):
+    q, k, _ = random_qkv(1, 4, 1, 257, 257, 128, dtype="bf16", seed=13)
+    v = torch.full((1, 1, 257, 128), c, dtype=torch.bfloat16)
+    o, _ = _gpu_forward(q, k, v, True, 0.0883883461356163)
+    err = (o.cpu().double() - c).abs().max().item()
+    assert err <= abs(c) * 2 ** -7, err   # within one bf16 ulp of c
+
+
+def test_causal_row_zero_is_first_value_row():
+    q, k, v = random_qkv(2, 8, 4, 130, 130, 128, dtype="bf16", seed=14)
+    o, _ = _gpu_forward(q, k, v, True, 0.0883883461356163)
+    assert torch.equal(o.cpu()[:, :, 0], v.repeat_interleave(2, dim=1)[:, :, 0])
+
+
+def test_gqa_equals_mha_with_repeated_kv_bitwise():
+    q, k, v = random_qkv(1, 8, 2, 300, 300, 128, dtype="bf16", seed=15)
+    o1, l1 = _gpu_forward(q, k, v, True, 0.0883883461356163)
+    o2, l2 = _gpu_forward(q, k.repeat_interleave(4, 1).contiguous(),
+                          v.repeat_interleave(4, 1).contiguous(), True, 0.0883883461356163)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_rows_sum_to_one_from_lse():
+    q, k, v = random_qkv(1, 4, 2, 200, 180, 128, dtype="bf16", seed=16)
+    scale = 0.0883883461356163
+    _, lse = _gpu_forward(q, k, v, True, scale)
+    s = torch.matmul(q.double(), k.double().repeat_interleave(2, 1).transpose(-1, -2).contiguous()) * scale
+    vis = torch.ones(200, 180, dtype=torch.bool).tril()
+    tot = (torch.exp(s - lse.cpu().double()[..., None]) * vis).sum(-1)
+    assert (tot - 1).abs().max().item() < 2e-3
+
+
+def test_deterministic_and_stream_ordered():
+    q, k, v = (t.cuda() for t in random_qkv(1, 8, 2, 520, 520, 128, dtype="bf16", seed=17))
+    o1, l1 = ta.forward(q, k, v, causal=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o2, l2 = ta.forward(q, k, v, causal=True, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_empty_query_set_is_a_noop():
+    q = torch.zeros(1, 4, 0, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 2, 5, 128, dtype=torch.bfloat16, device="cuda")
+    o, lse = ta.forward(q, k, k, causal=True)
+    assert o.shape == (1, 4, 0, 128) and lse.shape == (1, 4, 0)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size.
+# ---------------------------------------------------------------------------
+def _edge_rows(w, n_extra, seed):
+    """Flat row indices: first/last rows of heads, tile boundaries, plus random."""
+    rows = set()
+    for b in (0, w.B - 1):
+        for h in (0, w.Hq // 2, w.Hq - 1):
+            for i in (0, 1, 63, 64, 127, 128, w.Sq // 2, w.Sq - 2, w.Sq - 1):
+                if 0 <= i < w.Sq:
+                    rows.add((b * w.Hq + h) * w.Sq + i)
+    rng = np.random.default_rng(seed)
+    rows.update(rng.integers(0, w.B * w.Hq * w.Sq, size=n_extra).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "mha_bf16"])
+def test_workload_full_oracle(name):
+    w = WORKLOADS[name]
+    _say(f"workload {name}")
+    q, k, v = make_inputs(w)
+    o, lse = _gpu_forward(q, k, v, w.causal, w.scale)
+    o_ref, lse_ref = oracle.attention(q, k, v, w.scale, w.causal)
+    _check(o, lse, o_ref, lse_ref, w.dtype, name)
+
+
+@pytest.mark.parametrize("name", ["causal_mha_bf16", "causal_gqa_bf16", "longctx_gqa_bf16"])
+def test_workload_sampled_rows(name):
+    w = WORKLOADS[name]
+    _say(f"workload {name}")
+    if w.sample_rows:
+        q, k, v, rows = make_inputs(w, with_sample=True)
+        rows = np.union1d(rows, _edge_rows(w, 0, 0))
+    else:
+        q, k, v = make_inputs(w)
+        rows = _edge_rows(w, 512, w.seed)
+    o, lse = _gpu_forward(q, k, v, w.causal, w.scale)
+    o_rows = o.reshape(-1, w.D)[torch.as_tensor(rows, device="cuda")]
+    l_rows = lse.reshape(-1)[torch.as_tensor(rows, device="cuda")]
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, w.scale, w.causal, rows)
+    _check(o_rows, l_rows, o_ref, lse_ref, w.dtype, f"{name} ({len(rows)} rows)")
+    # Properties over every row: finite, and causal row 0 equals v[0].
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    if w.causal:
+        G = w.Hq // w.Hkv
+        v0 = v[:, :, 0].to("cuda").repeat_interleave(G, dim=1)
+        assert torch.equal(o[:, :, 0], v0)

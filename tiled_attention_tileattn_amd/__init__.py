@@ -1,0 +1,20 @@
+"""tileattn: exact attention forward for MI355X (gfx950), HIP kernels behind a C ABI.
+
+``forward(q, k, v, causal, scale) -> (o, lse)`` is the torch-facing entry;
+``tileattn_fwd`` / ``tileattn_fwd_f32`` / ``tileattn_strerror`` /
+``tileattn_launch_shape`` mirror the C functions of ``include/tileattn.h``.
+The shared library is loaded on first use and must have been built
+(``python -m tiled_attention_tileattn_amd.build``); there is no fallback.
+"""
+
+from .binding import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    TileAttnError,
+    forward,
+    load_library,
+    tileattn_fwd,
+    tileattn_fwd_f32,
+    tileattn_launch_shape,
+    tileattn_strerror,
+)

@@ -1,0 +1,136 @@
+"""Thin ctypes binding of ``libtileattn.so`` (argument marshalling only).
+
+The raw functions mirror the C ABI of ``include/tileattn.h`` name for name and
+take plain integers for device pointers and the stream.  ``forward`` is the
+torch convenience wrapper: it checks tensors, allocates ``o``/``lse`` with
+torch (the library itself allocates nothing) and passes torch's current HIP
+stream.  Every step of the attention runs in the library's kernels; there is
+no fallback of any kind -- if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtileattn.so")
+
+EXPORTED = ("tileattn_fwd", "tileattn_fwd_f32", "tileattn_strerror", "tileattn_launch_shape")
+
+STATUS = {
+    0: "TILEATTN_OK",
+    -1: "TILEATTN_ERR_NULL_POINTER",
+    -2: "TILEATTN_ERR_BAD_SHAPE",
+    -3: "TILEATTN_ERR_GQA_RATIO",
+    -4: "TILEATTN_ERR_HEAD_DIM",
+    -5: "TILEATTN_ERR_SCALE",
+    -6: "TILEATTN_ERR_ALIGNMENT",
+    -7: "TILEATTN_ERR_TOO_LARGE",
+    -8: "TILEATTN_ERR_LAUNCH",
+}
+
+_lib = None
+
+
+class TileAttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({tileattn_strerror(code)})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first "
+            "(python -m tiled_attention_tileattn_amd.build)")
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    sig = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.tileattn_fwd.argtypes = sig
+    lib.tileattn_fwd.restype = i
+    lib.tileattn_fwd_f32.argtypes = sig
+    lib.tileattn_fwd_f32.restype = i
+    lib.tileattn_strerror.argtypes = [i]
+    lib.tileattn_strerror.restype = ctypes.c_char_p
+    lib.tileattn_launch_shape.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i),
+                                          ctypes.POINTER(i), ctypes.POINTER(ctypes.c_longlong)]
+    lib.tileattn_launch_shape.restype = i
+    _lib = lib
+    return lib
+
+
+# ---- raw C-ABI mirrors (integers for pointers and stream) -------------------
+def tileattn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream) -> int:
+    return load_library().tileattn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D,
+                                       float(scale), int(bool(causal)), stream)
+
+
+def tileattn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream) -> int:
+    return load_library().tileattn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D,
+                                           float(scale), int(bool(causal)), stream)
+
+
+def tileattn_strerror(status: int) -> str:
+    return load_library().tileattn_strerror(int(status)).decode()
+
+
+def tileattn_launch_shape(dtype_bytes, B, Hq, Hkv, Sq, Sk, D, causal):
+    """Return (status, block_m, block_n, workgroups)."""
+    bm, bn, wg = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_longlong(0)
+    st = load_library().tileattn_launch_shape(dtype_bytes, B, Hq, Hkv, Sq, Sk, D, int(bool(causal)),
+                                              ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(wg))
+    return st, bm.value, bn.value, wg.value
+
+
+# ---- torch convenience wrapper ----------------------------------------------
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+            stream=None):
+    """Attention forward on the GPU: returns (o, lse).
+
+    q [B, Hq, Sq, D], k/v [B, Hkv, Sk, D]: contiguous bf16 (or fp32) tensors on
+    one HIP device.  ``scale`` defaults to 1/sqrt(D).  ``out``/``lse`` may be
+    preallocated ([B, Hq, Sq, D] in q's dtype, [B, Hq, Sq] fp32).  ``stream``
+    is a torch stream (default: the current stream of q's device).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D torch tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must share one dtype, bfloat16 or float32")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, Sq] on q's device")
+    fn = tileattn_fwd if q.dtype == torch.bfloat16 else tileattn_fwd_f32
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, Hq, Hkv, Sq, Sk, D, scale, causal, s.cuda_stream)
+    if rc != 0:
+        raise TileAttnError(rc, fn.__name__)
+    return out, lse

@@ -1,0 +1,644 @@
+// tileattn — exact attention forward for MI355X (gfx950 / CDNA4).
+//
+// Method: the tiled flash-attention loop of "Guia Prático de Programação de GPU
+// com Tiles: de Kernels cuTile e Triton ao Flash Attention" (Passo a Passo,
+// step 6 "Flash Attention — Softmax Online"): a block of query rows stays
+// resident, key/value tiles stream past it, and per tile the kernel
+//   (1) forms the scores of the query block against the key tile,
+//   (2) raises the running row maximum,
+//   (3) exponentiates the shifted scores,
+//   (4) rescales the running sum and the output accumulator by
+//       exp(old max - new max) and adds the new tile's contribution, with the
+//       probabilities cast to the value dtype before the second product,
+// and divides the accumulator by the running sum at the end.  Both products
+// accumulate in fp32 (step 5 "Multiplicação de Matrizes Tiled" and the
+// Troubleshooting note on fp16 accumulators).
+//
+// CDNA4 mapping (our design, not the pages'):
+//   * One workgroup = 4 waves = 128 query rows of one (batch, query head);
+//     each wave owns 32 query rows for the whole key loop.
+//   * The kernel computes the transposed products S^T = K * Q^T and
+//     O^T = V^T * P^T with v_mfma_f32_32x32x16_bf16.  In the 32x32 result
+//     layout a lane holds 16 entries of ONE output column, so with queries as
+//     columns every lane owns one query row: the row max and row sum are
+//     in-lane reductions plus one v_permlane32_swap between the two lanes
+//     that share the row, and the rescale factor is a per-lane scalar.
+//   * The fp32 S^T tile, once exponentiated and packed to bf16, is already
+//     in the B-operand layout of the P*V product (no LDS round trip); V is
+//     stored transposed in LDS with the key order permuted to match it.
+//   * Q lives in VGPRs for the whole loop (B operand of the first product).
+//   * K and V^T tiles are double-buffered in LDS; the next tile's global
+//     loads are issued before the current tile's math and written to the
+//     other buffer after it.  K rows are XOR-swizzled in 16-byte chunks so
+//     the 32 rows one MFMA operand read touches fall in distinct banks.
+//   * exp is computed as exp2 with scale*log2(e) folded into one FMA.
+//   * Causal: tiles entirely above the diagonal are never loaded; a wave whose
+//     rows see no key of a tile skips its math; masking code runs only on the
+//     diagonal tile(s) and the ragged last key tile.
+//   * Workgroup ids are remapped so the workgroups that one XCD (8 per chip,
+//     ids dealt round-robin) runs share a key/value head and read its K/V
+//     tiles from that XCD's L2; causal query tiles go heaviest first.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "../../include/tileattn.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRowsPerWave = 32;                       // query rows owned by one wave
+constexpr int kBlockN = 64;                            // keys per tile (bf16 path)
+constexpr int kF32Waves = 4;                           // fp32 path: waves per workgroup
+constexpr int kF32Threads = kF32Waves * 64;
+constexpr int kF32BlockM = kF32Waves * kRowsPerWave;   // fp32 path: 128 query rows
+constexpr int kBlockNF32 = 32;                         // keys per tile (fp32 path)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float wave_pair_max(float x) {
+  // Lanes l and l^32 hold the same query row; combine their partial maxima.
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float wave_pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Steps (2)-(3) of the tile update for one lane's 32 scores of its query row:
+// raise the running max, return the rescale factor alpha = exp(old - new)
+// (scaled units), overwrite the scores with p = exp2(s*c - m*c) and fold
+// their sum into the lane's running sum.  MASKED tiles carry -inf scores,
+// which must give p = 0 even when c = 0.
+template <bool MASKED>
+__device__ __forceinline__ float online_softmax_step(f32x16 (&s)[2], float& m_run, float& l_run,
+                                                     float c) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  mx = wave_pair_max(mx);
+  const float m_new = fmaxf(m_run, mx);
+  const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+  m_run = m_new;
+  const float mc = m_new * c;
+  float psum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x = s[kb][r];
+      float p = __builtin_amdgcn_exp2f(fmaf(x, c, -mc));
+      if (MASKED) p = (x == -INFINITY) ? 0.f : p;
+      s[kb][r] = p;
+      psum += p;
+    }
+  l_run = l_run * alpha + psum;
+  return alpha;
+}
+
+// Map a hardware workgroup id to (batch, query head, query tile).  Ids are
+// dealt to the 8 XCDs round-robin; the remap gives each XCD a contiguous range
+// of the logical order (batch, kv head, query tile [heaviest first if causal],
+// query head within the group), so an XCD's resident workgroups share K/V.
+__device__ __forceinline__ void map_workgroup(int hw_id, int nwg, int Hkv, int G, int nqt,
+                                              bool causal, int& b, int& hq, int& qt) {
+  int logical = hw_id;
+  if ((nwg & 7) == 0) {
+    const int per_xcd = nwg >> 3;
+    logical = (hw_id & 7) * per_xcd + (hw_id >> 3);
+  }
+  const int g = logical % G;
+  int rest = logical / G;
+  const int tq = rest % nqt;
+  rest /= nqt;
+  const int hk = rest % Hkv;
+  b = rest / Hkv;
+  hq = hk * G + g;
+  qt = causal ? (nqt - 1 - tq) : tq;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel
+// ---------------------------------------------------------------------------
+#ifndef TILEATTN_BF16_WAVES
+#define TILEATTN_BF16_WAVES 8
+#endif
+#ifndef TILEATTN_RESCALE_THRESHOLD
+#define TILEATTN_RESCALE_THRESHOLD 8.0f
+#endif
+#ifndef TILEATTN_SETPRIO
+#define TILEATTN_SETPRIO 1
+#endif
+
+template <int D>
+struct Bf16Tile {
+  static constexpr int kWaves = TILEATTN_BF16_WAVES;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kBlockM = kWaves * kRowsPerWave;  // query rows per workgroup
+  static constexpr int kChunks = D / 8;                    // 16-byte chunks per K/V row
+  // LDS row pitches (bytes).  K rows are padded by 16 bytes: the 16 rows of
+  // one K-operand read phase (same 16-byte chunk of consecutive keys) then
+  // start 16 bytes apart modulo 256 and hit distinct banks.  V rows are
+  // padded by 64 bytes: one phase of the transposed V read touches 4
+  // consecutive keys x 64 contiguous bytes, which then tile 256 bytes
+  // exactly.  Padding (rather than an XOR swizzle) keeps every operand
+  // address of a lane a compile-time offset from one base register.
+  static constexpr int kKPitch = D * 2 + 16;
+  static constexpr int kVPitch = D * 2 + 64;
+  static constexpr int kKBytes = kBlockN * kKPitch;
+  static constexpr int kVBytes = kBlockN * kVPitch;
+  static constexpr int kStageBytes = kKBytes + kVBytes;    // K tile then V tile
+  static constexpr int kLoads = kBlockN * kChunks / kThreads;  // 16-byte loads per tensor
+  static_assert(kLoads >= 1 && kLoads * kThreads == kBlockN * kChunks, "tile/threads mismatch");
+};
+
+// Steps (2)-(4a) of the tile update for one lane's 32 scores of its query row.
+// The reference max m_run is raised only when some row's tile max exceeds it
+// by more than TILEATTN_RESCALE_THRESHOLD (log2 units; a wave-uniform branch),
+// which leaves the result exact: numerator and denominator are accumulated
+// against the same m_run, and p <= 2^threshold stays far from fp32/bf16
+// overflow.  When the branch is taken every lane rescales its accumulator and
+// running sum by alpha = exp2((m_old - m_new) * c).  The running sum adds the
+// fp32 p; p is then packed to bf16 (round to nearest even) in the B-operand
+// layout of the P*V product.  MASKED tiles carry -inf scores, which must give
+// p = 0 even when c = 0.
+template <bool MASKED, int NACC>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& m_run, float& l_run,
+                                             float c, f32x16 (&acc)[NACC],
+                                             bf16x8 (&pf)[2][2]) {
+  float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+  mx = wave_pair_max(mx);
+  const bool grow = (m_run == -INFINITY) || ((mx - m_run) * c > TILEATTN_RESCALE_THRESHOLD);
+  if (__ballot(grow)) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) acc[i] *= alpha;
+  }
+  const float mc = m_run * c;
+  float psum0 = 0.f, psum1 = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float x0 = s[kb][8 * t + e], x1 = s[kb][8 * t + e + 1];
+        float p0 = __builtin_amdgcn_exp2f(fmaf(x0, c, -mc));
+        float p1 = __builtin_amdgcn_exp2f(fmaf(x1, c, -mc));
+        if (MASKED) {
+          p0 = (x0 == -INFINITY) ? 0.f : p0;
+          p1 = (x1 == -INFINITY) ? 0.f : p1;
+        }
+        psum0 += p0;
+        psum1 += p1;
+        pf[kb][t][e] = (__bf16)p0;
+        pf[kb][t][e + 1] = (__bf16)p1;
+      }
+  l_run += psum0 + psum1;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    int Hq, int Hkv, int Sq, int Sk, float scale, int nqt, int nwg) {
+  using T = Bf16Tile<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;  // which 32-lane half
+  const int l32 = lane & 31;
+  const int wave = tid >> 6;
+  const int G = Hq / Hkv;
+
+  int b, hq, qt;
+  map_workgroup(blockIdx.x, nwg, Hkv, G, nqt, CAUSAL, b, hq, qt);
+  const int hk = hq / G;
+  const int q0 = qt * T::kBlockM;
+  const int qw = q0 + wave * kRowsPerWave;  // first query row of this wave
+  const int my_row = qw + l32;              // query row owned by this lane
+
+  const size_t q_head = ((size_t)b * Hq + hq) * (size_t)Sq;
+  const size_t kv_head = ((size_t)b * Hkv + hk) * (size_t)Sk;
+  const uint16_t* Kh = K + kv_head * D;
+  const uint16_t* Vh = V + kv_head * D;
+
+  // Key tiles this workgroup visits (causal: up to its last valid row).
+  int nkt = (Sk + kBlockN - 1) / kBlockN;
+  if (CAUSAL) {
+    const int last_row = min(q0 + T::kBlockM - 1, Sq - 1);
+    nkt = min(nkt, last_row / kBlockN + 1);
+  }
+
+  // ---- Q fragment: B operand of S^T = K Q^T (k = d, n = query) ------------
+  bf16x8 qf[D / 16];
+  {
+    const bool ok = my_row < Sq;
+    const uint16_t* qrow = Q + (q_head + (size_t)(ok ? my_row : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      uint4 u = ok ? *reinterpret_cast<const uint4*>(qrow + kk * 16 + half * 8)
+                   : make_uint4(0, 0, 0, 0);
+      qf[kk] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+
+  // ---- tile loaders: global -> registers -> LDS (row-major, swizzled) -----
+  uint4 kreg[T::kLoads], vreg[T::kLoads];
+  auto load_tile = [&](int j) {
+    const int key0 = j * kBlockN;
+#pragma unroll
+    for (int i = 0; i < T::kLoads; ++i) {
+      const int idx = tid + i * T::kThreads;
+      const int r = idx / T::kChunks, cc = idx % T::kChunks;  // coalesced along a row
+      const bool ok = key0 + r < Sk;
+      const size_t g = (size_t)(key0 + r) * D + cc * 8;
+      kreg[i] = ok ? *reinterpret_cast<const uint4*>(Kh + g) : make_uint4(0, 0, 0, 0);
+      vreg[i] = ok ? *reinterpret_cast<const uint4*>(Vh + g) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_tile = [&](int stage) {
+    unsigned char* ks = smem + stage * T::kStageBytes;
+    unsigned char* vs = ks + T::kKBytes;
+#pragma unroll
+    for (int i = 0; i < T::kLoads; ++i) {
+      const int idx = tid + i * T::kThreads;
+      const int r = idx / T::kChunks, cc = idx % T::kChunks;
+      *reinterpret_cast<uint4*>(ks + r * T::kKPitch + cc * 16) = kreg[i];
+      *reinterpret_cast<uint4*>(vs + r * T::kVPitch + cc * 16) = vreg[i];
+    }
+  };
+
+  // Per-lane byte offsets of the operand reads (tile-independent).
+  // K (A operand of S^T): row kb*32 + l32, bytes 32*kk + 16*half.
+  // V (A operand of O^T, read transposed with ds_read_b64_tr_b16): in each
+  // 16-lane group, source lane s reads 4 consecutive d of key row
+  // (s >> 2); output lane 4a+b then holds d = 4a+b of 4 consecutive keys.
+  // The key rows of one read are kb*32 + 16t + 8rd + 4*half + (s >> 2), so
+  // lanes 0-31 receive keys {0-3, 8-11} and lanes 32-63 keys {4-7, 12-15} of
+  // each 16-key step: exactly the k order of the P^T operand built from the
+  // S^T accumulator layout.
+  const int s16 = lane & 15;
+  const int k_lane_off = l32 * T::kKPitch + 16 * half;
+  const int v_lane_off = (4 * half + (s16 >> 2)) * T::kVPitch +
+                         2 * (16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
+
+  // ---- running state (per lane: one query row, half of its keys) ----------
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+  float m_run = -INFINITY;  // reference max of raw scores q.k
+  float l_run = 0.f;        // this lane's partial running sum
+  const float c = scale * kLog2e;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < nkt; ++j) {
+    const int stage = j & 1;
+    const bool has_next = (j + 1) < nkt;
+    if (has_next) load_tile(j + 1);
+
+    const int key0 = j * kBlockN;
+    const bool wave_active = !CAUSAL || key0 <= qw + kRowsPerWave - 1;
+    if (wave_active) {
+      const unsigned char* ks = smem + stage * T::kStageBytes + k_lane_off;
+      const unsigned char* vs = smem + stage * T::kStageBytes + T::kKBytes + v_lane_off;
+
+      // (1) S^T = K Q^T: two 32-key blocks, fp32 accumulation.
+      if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8*>(ks + kb * 32 * T::kKPitch + kk * 32);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+        }
+      }
+      if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+
+      // (2)-(4a) mask (diagonal / ragged tiles only), online softmax, pack P.
+      bf16x8 pf[2][2];
+      const bool need_mask = (CAUSAL && key0 + kBlockN - 1 > qw) || (key0 + kBlockN > Sk);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool vis = key < Sk && (!CAUSAL || key <= my_row);
+            s[kb][r] = vis ? s[kb][r] : -INFINITY;
+          }
+        softmax_tile<true>(s, m_run, l_run, c, acc, pf);
+      } else {
+        softmax_tile<false>(s, m_run, l_run, c, acc, pf);
+      }
+
+      // (4b) acc += V^T P^T.
+      if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            typedef short i16x4 __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+            const int o0 = (kb * 32 + 16 * t) * T::kVPitch + db * 64;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(uintptr_t)(vs + o0));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(uintptr_t)(vs + o0 + 8 * T::kVPitch));
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][t], acc[db], 0, 0, 0);
+          }
+      if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    }
+
+    if (has_next) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, lse = m*scale + ln l --------------------------
+  const float l_tot = wave_pair_sum(l_run);
+  const float inv = 1.0f / l_tot;
+  if (my_row < Sq) {
+    uint16_t* orow = O + (q_head + my_row) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        __bf16 o4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[db][4 * g + e] * inv);
+        uint2 u;
+        u.x = (uint32_t)__builtin_bit_cast(uint16_t, o4[0]) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, o4[1]) << 16);
+        u.y = (uint32_t)__builtin_bit_cast(uint16_t, o4[2]) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, o4[3]) << 16);
+        *reinterpret_cast<uint2*>(orow + db * 32 + 8 * g + 4 * half) = u;
+      }
+    if (half == 0) LSE[q_head + my_row] = m_run * scale + logf(l_tot);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: same structure, v_mfma_f32_32x32x2_f32, 32-key tiles, P in fp32.
+// ---------------------------------------------------------------------------
+template <int D>
+struct F32Layout {
+  static constexpr int kPitch = D + 1;                       // floats per LDS row (pad: banks)
+  static constexpr int kTileFloats = kBlockNF32 * kPitch;
+  static constexpr int kLoadsPerThread = kBlockNF32 * D / 4 / kF32Threads;  // float4 loads
+  static_assert(kLoadsPerThread * kF32Threads * 4 == kBlockNF32 * D, "tile/threads mismatch");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kF32Threads) void attn_fwd_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Sq, int Sk,
+    float scale, int nqt, int nwg) {
+  using L = F32Layout<D>;
+  __shared__ float ks[L::kTileFloats];
+  __shared__ float vs[L::kTileFloats];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int wave = tid >> 6;
+  const int G = Hq / Hkv;
+
+  int b, hq, qt;
+  map_workgroup(blockIdx.x, nwg, Hkv, G, nqt, CAUSAL, b, hq, qt);
+  const int hk = hq / G;
+  const int q0 = qt * kF32BlockM;
+  const int qw = q0 + wave * kRowsPerWave;
+  const int my_row = qw + l32;
+
+  const size_t q_head = ((size_t)b * Hq + hq) * (size_t)Sq;
+  const size_t kv_head = ((size_t)b * Hkv + hk) * (size_t)Sk;
+  const float* Kh = K + kv_head * D;
+  const float* Vh = V + kv_head * D;
+
+  int nkt = (Sk + kBlockNF32 - 1) / kBlockNF32;
+  if (CAUSAL) {
+    const int last_row = min(q0 + kF32BlockM - 1, Sq - 1);
+    nkt = min(nkt, last_row / kBlockNF32 + 1);
+  }
+
+  // Q fragment: B operand (k = d, n = query); lane holds d = 2*kk + half.
+  float qf[D / 2];
+  {
+    const bool ok = my_row < Sq;
+    const float* qrow = Q + (q_head + (size_t)(ok ? my_row : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 2; ++kk) qf[kk] = ok ? qrow[2 * kk + half] : 0.f;
+  }
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = scale * kLog2e;
+
+  for (int j = 0; j < nkt; ++j) {
+    const int key0 = j * kBlockNF32;
+    __syncthreads();  // previous tile fully consumed
+#pragma unroll
+    for (int i = 0; i < L::kLoadsPerThread; ++i) {
+      const int idx = tid + i * kF32Threads;
+      const int r = idx / (D / 4), c4 = idx % (D / 4);
+      float4 kv4 = make_float4(0.f, 0.f, 0.f, 0.f), vv4 = kv4;
+      if (key0 + r < Sk) {
+        kv4 = *reinterpret_cast<const float4*>(Kh + (size_t)(key0 + r) * D + c4 * 4);
+        vv4 = *reinterpret_cast<const float4*>(Vh + (size_t)(key0 + r) * D + c4 * 4);
+      }
+      float* kd = ks + r * L::kPitch + c4 * 4;
+      float* vd = vs + r * L::kPitch + c4 * 4;
+      kd[0] = kv4.x; kd[1] = kv4.y; kd[2] = kv4.z; kd[3] = kv4.w;
+      vd[0] = vv4.x; vd[1] = vv4.y; vd[2] = vv4.z; vd[3] = vv4.w;
+    }
+    __syncthreads();
+
+    const bool wave_active = !CAUSAL || key0 <= qw + kRowsPerWave - 1;
+    if (!wave_active) continue;
+
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 2; ++kk) {
+      const float a = ks[l32 * L::kPitch + 2 * kk + half];
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[kk], s, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      const bool vis = key < Sk && (!CAUSAL || key <= my_row);
+      s[r] = vis ? s[r] : -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = wave_pair_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f((m_run - m_new) * c);
+    m_run = m_new;
+    const float mc = m_new * c;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x = s[r];
+      const float p = (x == -INFINITY) ? 0.f : exp2f(fmaf(x, c, -mc));
+      s[r] = p;
+      psum += p;
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      acc[db] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * half + (r & 3);
+        const float a = vs[key * L::kPitch + db * 32 + l32];
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[r], acc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  const float l_tot = wave_pair_sum(l_run);
+  const float inv = 1.0f / l_tot;
+  if (my_row < Sq) {
+    float* orow = O + (q_head + my_row) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4 u = make_float4(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
+                               acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+        *reinterpret_cast<float4*>(orow + db * 32 + 8 * g + 4 * half) = u;
+      }
+    if (half == 0) LSE[q_head + my_row] = m_run * scale + logf(l_tot);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: validation and launch.
+// ---------------------------------------------------------------------------
+int validate(const void* q, const void* k, const void* v, const void* o, const void* lse,
+             int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale, bool* empty) {
+  *empty = false;
+  if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1 || Sk < 1) return TILEATTN_ERR_BAD_SHAPE;
+  if (Hq % Hkv != 0) return TILEATTN_ERR_GQA_RATIO;
+  if (D != 64 && D != 128) return TILEATTN_ERR_HEAD_DIM;
+  if (!(scale >= 0.f) || isinf(scale)) return TILEATTN_ERR_SCALE;
+  // 64-bit index range: elements of q/o and of k/v, and the workgroup count.
+  const double q_elems = (double)B * Hq * Sq * D;
+  const double kv_elems = (double)B * Hkv * Sk * D;
+  const double nwg = (double)B * Hq * ((Sq + kF32BlockM - 1) / kF32BlockM);  // smallest block_m
+  if (q_elems > 9.0e18 || kv_elems > 9.0e18 || nwg > 2147483647.0) return TILEATTN_ERR_TOO_LARGE;
+  if (B == 0 || Hq == 0 || Sq == 0) {
+    *empty = true;
+    return TILEATTN_OK;
+  }
+  if (!q || !k || !v || !o || !lse) return TILEATTN_ERR_NULL_POINTER;
+  auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
+    return TILEATTN_ERR_ALIGNMENT;
+  return TILEATTN_OK;
+}
+
+template <int BLOCK_M, int THREADS, typename Kern, typename TIn, typename TOut>
+int launch(Kern kernel, const TIn* q, const TIn* k, const TIn* v, TOut* o, float* lse, int B,
+           int Hq, int Hkv, int Sq, int Sk, float scale, void* stream) {
+  const int nqt = (Sq + BLOCK_M - 1) / BLOCK_M;
+  const int nwg = B * Hq * nqt;
+  void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&Hq,
+                  (void*)&Hkv, (void*)&Sq, (void*)&Sk, (void*)&scale, (void*)&nqt, (void*)&nwg};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(nwg), dim3(THREADS),
+                                 args, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TILEATTN_OK : TILEATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int tileattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                            int causal, void* stream) {
+  bool empty;
+  const int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty);
+  if (st != TILEATTN_OK || empty) return st;
+  auto qq = static_cast<const uint16_t*>(q), kk = static_cast<const uint16_t*>(k),
+       vv = static_cast<const uint16_t*>(v);
+  auto oo = static_cast<uint16_t*>(o);
+  using T128 = Bf16Tile<128>;
+  using T64 = Bf16Tile<64>;
+  if (D == 128)
+    return causal ? launch<T128::kBlockM, T128::kThreads>(attn_fwd_bf16_kernel<128, true>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream)
+                  : launch<T128::kBlockM, T128::kThreads>(attn_fwd_bf16_kernel<128, false>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream);
+  return causal ? launch<T64::kBlockM, T64::kThreads>(attn_fwd_bf16_kernel<64, true>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream)
+                : launch<T64::kBlockM, T64::kThreads>(attn_fwd_bf16_kernel<64, false>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream);
+}
+
+extern "C" int tileattn_fwd_f32(const float* q, const float* k, const float* v, float* o,
+                                float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                float scale, int causal, void* stream) {
+  bool empty;
+  const int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty);
+  if (st != TILEATTN_OK || empty) return st;
+  if (D == 128)
+    return causal ? launch<kF32BlockM, kF32Threads>(attn_fwd_f32_kernel<128, true>, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, stream)
+                  : launch<kF32BlockM, kF32Threads>(attn_fwd_f32_kernel<128, false>, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, stream);
+  return causal ? launch<kF32BlockM, kF32Threads>(attn_fwd_f32_kernel<64, true>, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, stream)
+                : launch<kF32BlockM, kF32Threads>(attn_fwd_f32_kernel<64, false>, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, stream);
+}
+
+extern "C" const char* tileattn_strerror(int status) {
+  switch (status) {
+    case TILEATTN_OK: return "ok";
+    case TILEATTN_ERR_NULL_POINTER: return "a tensor pointer is NULL";
+    case TILEATTN_ERR_BAD_SHAPE: return "bad shape: sizes must be >= 0, Hkv >= 1 and Sk >= 1";
+    case TILEATTN_ERR_GQA_RATIO: return "Hq must be a multiple of Hkv";
+    case TILEATTN_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";
+    case TILEATTN_ERR_SCALE: return "scale must be finite and >= 0";
+    case TILEATTN_ERR_ALIGNMENT: return "tensor pointers must be 16-byte aligned";
+    case TILEATTN_ERR_TOO_LARGE: return "problem exceeds the index range";
+    case TILEATTN_ERR_LAUNCH: return "kernel launch failed (is a gfx950 device current?)";
+    default: return "unknown tileattn status";
+  }
+}
+
+extern "C" int tileattn_launch_shape(int dtype_bytes, int B, int Hq, int Hkv, int Sq, int Sk,
+                                     int D, int causal, int* block_m, int* block_n,
+                                     long long* workgroups) {
+  (void)causal;
+  if (dtype_bytes != 2 && dtype_bytes != 4) return TILEATTN_ERR_BAD_SHAPE;
+  bool empty;
+  // Shape checks only: pass dummy aligned non-null pointers.
+  static const float dummy[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
+  const int st = validate(dummy, dummy, dummy, dummy, dummy, B, Hq, Hkv, Sq, Sk, D, 1.0f, &empty);
+  if (st != TILEATTN_OK) return st;
+  const int bm = dtype_bytes == 2 ? (D == 128 ? Bf16Tile<128>::kBlockM : Bf16Tile<64>::kBlockM)
+                                  : kF32BlockM;
+  if (block_m) *block_m = bm;
+  if (block_n) *block_n = dtype_bytes == 2 ? kBlockN : kBlockNF32;
+  if (workgroups) *workgroups = empty ? 0 : (long long)B * Hq * ((Sq + bm - 1) / bm);
+  return TILEATTN_OK;
+}
