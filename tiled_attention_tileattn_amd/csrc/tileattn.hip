@@ -50,6 +50,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Native vector type for 16-byte staging registers: arrays of HIP's uint4
+// wrapper struct are not always promoted to registers and can land in
+// scratch memory.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsPerWave = 32;                       // query rows owned by one wave
 constexpr int kBlockN = 64;                            // keys per tile (bf16 path)
@@ -180,7 +184,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& m_run, float
     for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
   mx = wave_pair_max(mx);
   const bool grow = (m_run == -INFINITY) || ((mx - m_run) * c > TILEATTN_RESCALE_THRESHOLD);
-  if (__ballot(grow)) {
+  if (__builtin_expect(__ballot(grow) != 0, 0)) {  // rare after the first tile
     const float m_new = fmaxf(m_run, mx);
     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
     m_run = m_new;
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
   }
 
   // ---- tile loaders: global -> registers -> LDS (row-major, swizzled) -----
-  uint4 kreg[T::kLoads], vreg[T::kLoads];
+  u32x4 kreg[T::kLoads], vreg[T::kLoads];
   auto load_tile = [&](int j) {
     const int key0 = j * kBlockN;
 #pragma unroll
@@ -268,8 +272,8 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
       const int r = idx / T::kChunks, cc = idx % T::kChunks;  // coalesced along a row
       const bool ok = key0 + r < Sk;
       const size_t g = (size_t)(key0 + r) * D + cc * 8;
-      kreg[i] = ok ? *reinterpret_cast<const uint4*>(Kh + g) : make_uint4(0, 0, 0, 0);
-      vreg[i] = ok ? *reinterpret_cast<const uint4*>(Vh + g) : make_uint4(0, 0, 0, 0);
+      kreg[i] = ok ? *reinterpret_cast<const u32x4*>(Kh + g) : u32x4{0, 0, 0, 0};
+      vreg[i] = ok ? *reinterpret_cast<const u32x4*>(Vh + g) : u32x4{0, 0, 0, 0};
     }
   };
   auto store_tile = [&](int stage) {
@@ -279,8 +283,8 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
     for (int i = 0; i < T::kLoads; ++i) {
       const int idx = tid + i * T::kThreads;
       const int r = idx / T::kChunks, cc = idx % T::kChunks;
-      *reinterpret_cast<uint4*>(ks + r * T::kKPitch + cc * 16) = kreg[i];
-      *reinterpret_cast<uint4*>(vs + r * T::kVPitch + cc * 16) = vreg[i];
+      *reinterpret_cast<u32x4*>(ks + r * T::kKPitch + cc * 16) = kreg[i];
+      *reinterpret_cast<u32x4*>(vs + r * T::kVPitch + cc * 16) = vreg[i];
     }
   };
 
@@ -339,18 +343,24 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
       bf16x8 pf[2][2];
       const bool need_mask = (CAUSAL && key0 + kBlockN - 1 > qw) || (key0 + kBlockN > Sk);
       if (need_mask) {
+        // Entry r of block kb is key key0 + kb*32 + 8*(r>>2) + 4*half + (r&3);
+        // it is visible iff that key <= min(Sk - 1, my_row) (causal) or
+        // <= Sk - 1: one per-lane limit against compile-time offsets.
+        const int lim = (CAUSAL ? min(Sk - 1, my_row) : Sk - 1) - key0 - 4 * half;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool vis = key < Sk && (!CAUSAL || key <= my_row);
-            s[kb][r] = vis ? s[kb][r] : -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r)
+            s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) <= lim) ? s[kb][r] : -INFINITY;
         softmax_tile<true>(s, m_run, l_run, c, acc, pf);
       } else {
         softmax_tile<false>(s, m_run, l_run, c, acc, pf);
       }
+
+      // Without the causal branch around the tile body the scheduler
+      // overlaps the softmax with the P*V operand reads far enough to spill;
+      // a fence between the two keeps the live ranges apart.
+      if constexpr (!CAUSAL) __builtin_amdgcn_sched_barrier(0);
 
       // (4b) acc += V^T P^T.
       if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);

@@ -1,0 +1,146 @@
+"""Summarise rocprofv3 CSV output for the attention kernel into a short markdown file.
+
+    python3 -m tiled_attention_tileattn_amd.rocprof_summary OUT_DIR \
+        --trace DIR --fetch DIR --write DIR --sq DIR --copy-fetch DIR --copy-write DIR \
+        --out profiles/NAME.md --commands "cmd1" "cmd2" ...
+
+Each DIR is a ``rocprofv3 -f csv -d DIR -o run`` output directory of one pass
+(kernel trace with --stats; then one --pmc pass per counter group).  The copy
+passes profile ``bench.py --copy-calibration`` (a plain 256 MiB device copy):
+what FETCH_SIZE / WRITE_SIZE read for it gives the factor that turns those
+counters into bytes.  The summary ends with a JSON block of the figures that
+``bench.py`` reads (it uses them only while the kernel source still has the
+hash recorded here).
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+KERNEL_KEY = "attn_fwd_bf16_kernel<128, true>"
+COPY_BYTES = 256 * 1024 * 1024
+SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "tileattn.hip")
+
+
+def source_hash(path: str = SRC) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _csv(d: str, suffix: str):
+    paths = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not paths:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    with open(paths[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def counters(d: str, key: str):
+    """Mean per-dispatch value of each counter for kernels whose name contains key."""
+    acc = {}
+    for r in _csv(d, "counter_collection.csv"):
+        if key in r["Kernel_Name"]:
+            acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: statistics.fmean(v) for k, v in acc.items()}
+
+
+def trace_stats(d: str, key: str):
+    for r in _csv(d, "kernel_stats.csv"):
+        if key in r["Name"]:
+            return {"calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
+                    "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])}
+    raise KeyError(key)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    for k in ("trace", "fetch", "write", "sq", "copy-fetch", "copy-write"):
+        ap.add_argument(f"--{k}", required=True)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--workload", default="causal_gqa_bf16 (B=1, Hq=32, Hkv=8, S=8192, D=128)")
+    ap.add_argument("--flop", type=float, default=549755813888.0)
+    ap.add_argument("--compulsory-bytes", type=float, default=168820736.0)
+    ap.add_argument("--commands", nargs="*", default=[])
+    a = ap.parse_args()
+
+    tr = trace_stats(a.trace, KERNEL_KEY)
+    fetch_kib = counters(a.fetch, KERNEL_KEY)["FETCH_SIZE"]
+    write_kib = counters(a.write, KERNEL_KEY)["WRITE_SIZE"]
+    sq = counters(a.sq, KERNEL_KEY)
+    cf = counters(a.copy_fetch, "copyBuffer").get("FETCH_SIZE") or \
+        counters(a.copy_fetch, "elementwise")["FETCH_SIZE"]
+    cw = counters(a.copy_write, "copyBuffer").get("WRITE_SIZE") or \
+        counters(a.copy_write, "elementwise")["WRITE_SIZE"]
+    f_scale = COPY_BYTES / (cf * 1024.0)
+    w_scale = COPY_BYTES / (cw * 1024.0)
+    fetch_b = fetch_kib * 1024.0 * f_scale
+    write_b = write_kib * 1024.0 * w_scale
+    avg_s = tr["avg_ns"] * 1e-9
+    gui = sq.get("GRBM_GUI_ACTIVE", float("nan"))
+    xcds = 8
+    simds = 1024
+    mfma_util = sq.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (gui / xcds * simds)
+    lds_conf = sq.get("SQ_LDS_BANK_CONFLICT", float("nan")) / max(sq.get("SQ_LDS_IDX_ACTIVE", 1.0), 1.0)
+    fig = {
+        "kernel": KERNEL_KEY,
+        "workload": a.workload,
+        "source_sha256_16": source_hash(),
+        "avg_kernel_ns": tr["avg_ns"],
+        "calls": tr["calls"],
+        "tflops_at_avg": a.flop / avg_s / 1e12,
+        "fetch_bytes": fetch_b,
+        "write_bytes": write_b,
+        "traffic_bytes": fetch_b + write_b,
+        "compulsory_bytes": a.compulsory_bytes,
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "mfma_busy_frac": mfma_util,
+        "lds_bank_conflict_per_active": lds_conf,
+        "effective_clock_ghz": (gui / xcds) / avg_s / 1e9,
+        "valu_insts": sq.get("SQ_INSTS_VALU"),
+        "mfma_insts": sq.get("SQ_INSTS_MFMA"),
+        "lds_insts": sq.get("SQ_INSTS_LDS"),
+    }
+    lines = [
+        f"# rocprofv3: {KERNEL_KEY}, {a.workload}",
+        "",
+        "Kernel-trace and counter summary of one `bench.py` run (one launch = the whole",
+        "attention forward of the workload).  Counter passes are separate runs.",
+        "",
+        "| figure | value |",
+        "|---|---|",
+        f"| dispatches profiled | {tr['calls']} |",
+        f"| average kernel time | {tr['avg_ns']/1e3:.1f} us (min {tr['min_ns']/1e3:.1f}, max {tr['max_ns']/1e3:.1f}) |",
+        f"| TFLOP/s at the average (counted FLOP {a.flop:.4g}) | {fig['tflops_at_avg']:.1f} |",
+        f"| HBM fetch (FETCH_SIZE x {f_scale:.3f}) | {fetch_b/2**20:.1f} MiB |",
+        f"| HBM write (WRITE_SIZE x {w_scale:.3f}) | {write_b/2**20:.1f} MiB |",
+        f"| compulsory bytes (Q, K, V read; O, lse written) | {a.compulsory_bytes/2**20:.1f} MiB |",
+        f"| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/8 x 1024 SIMDs)) | {mfma_util*100:.1f} % |",
+        f"| LDS bank conflicts per active LDS cycle | {lds_conf:.4f} |",
+        f"| effective engine clock (GRBM_GUI_ACTIVE/8 / kernel time) | {fig['effective_clock_ghz']:.2f} GHz |",
+        f"| VALU / MFMA / LDS instructions | {fig['valu_insts']:.3g} / {fig['mfma_insts']:.3g} / {fig['lds_insts']:.3g} |",
+        f"| copy calibration (256 MiB copy): FETCH_SIZE / WRITE_SIZE | {cf:.0f} KiB / {cw:.0f} KiB |",
+        "",
+        "Commands (run from the repository root, `export TMPDIR=/tmp`):",
+        "",
+    ] + [f"    {c}" for c in a.commands] + [
+        "",
+        "```json",
+        json.dumps(fig, indent=1),
+        "```",
+        "",
+    ]
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()
