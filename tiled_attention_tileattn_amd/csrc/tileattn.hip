@@ -140,6 +140,14 @@ __device__ __forceinline__ void map_workgroup(int hw_id, int nwg, int Hkv, int G
 #ifndef TILEATTN_SETPRIO
 #define TILEATTN_SETPRIO 1
 #endif
+// Depth (in MFMAs) of the LDS operand prefetch ring of each product.
+#ifndef TILEATTN_PREFETCH
+#define TILEATTN_PREFETCH 4
+#endif
+// 1: global->register tile loads clamp the row index (no branches).
+#ifndef TILEATTN_CLAMPED_LOADS
+#define TILEATTN_CLAMPED_LOADS 1
+#endif
 
 template <int D>
 struct Bf16Tile {
@@ -217,8 +225,8 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& m_run, float
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    const uint16_t* __restrict__ Q, const uint16_t* K,
+    const uint16_t* V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Hq, int Hkv, int Sq, int Sk, float scale, int nqt, int nwg) {
   using T = Bf16Tile<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::kStageBytes];
@@ -270,10 +278,18 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
     for (int i = 0; i < T::kLoads; ++i) {
       const int idx = tid + i * T::kThreads;
       const int r = idx / T::kChunks, cc = idx % T::kChunks;  // coalesced along a row
-      const bool ok = key0 + r < Sk;
-      const size_t g = (size_t)(key0 + r) * D + cc * 8;
-      kreg[i] = ok ? *reinterpret_cast<const u32x4*>(Kh + g) : u32x4{0, 0, 0, 0};
-      vreg[i] = ok ? *reinterpret_cast<const u32x4*>(Vh + g) : u32x4{0, 0, 0, 0};
+      if (TILEATTN_CLAMPED_LOADS) {
+        // Rows past the last key are clamped to it: those keys are masked to
+        // p = 0 and the clamped rows hold finite input data.
+        const size_t g = (size_t)min(key0 + r, Sk - 1) * D + cc * 8;
+        kreg[i] = *reinterpret_cast<const u32x4*>(Kh + g);
+        vreg[i] = *reinterpret_cast<const u32x4*>(Vh + g);
+      } else {
+        const bool ok = key0 + r < Sk;
+        const size_t g = (size_t)(key0 + r) * D + cc * 8;
+        kreg[i] = ok ? *reinterpret_cast<const u32x4*>(Kh + g) : u32x4{0, 0, 0, 0};
+        vreg[i] = ok ? *reinterpret_cast<const u32x4*>(Vh + g) : u32x4{0, 0, 0, 0};
+      }
     }
   };
   auto store_tile = [&](int stage) {
@@ -325,16 +341,26 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
       const unsigned char* ks = smem + stage * T::kStageBytes + k_lane_off;
       const unsigned char* vs = smem + stage * T::kStageBytes + T::kKBytes + v_lane_off;
 
-      // (1) S^T = K Q^T: two 32-key blocks, fp32 accumulation.
+      // (1) S^T = K Q^T: two 32-key blocks, fp32 accumulation.  MFMA i uses
+      // K operand i (kk = i/2, block i%2); operands are read from LDS
+      // TILEATTN_PREFETCH MFMAs ahead into a register ring, and each step is
+      // fenced so the scheduler cannot pull the reads back next to their use.
       if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
       f32x16 s[2] = {f32x16{}, f32x16{}};
+      {
+        constexpr int kN = 2 * (D / 16);
+        constexpr int kP = TILEATTN_PREFETCH;
+        bf16x8 ring[kP];
+        auto fetch = [&](int i) {
+          ring[i % kP] = *reinterpret_cast<const bf16x8*>(ks + (i & 1) * 32 * T::kKPitch + (i >> 1) * 32);
+        };
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
+        for (int i = 0; i < kP; ++i) fetch(i);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(ks + kb * 32 * T::kKPitch + kk * 32);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+        for (int i = 0; i < kN; ++i) {
+          s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kP], qf[i >> 1], s[i & 1], 0, 0, 0);
+          if (i + kP < kN) fetch(i + kP);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
@@ -362,24 +388,34 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
       // a fence between the two keeps the live ranges apart.
       if constexpr (!CAUSAL) __builtin_amdgcn_sched_barrier(0);
 
-      // (4b) acc += V^T P^T.
+      // (4b) acc += V^T P^T.  MFMA i = (16-key group g = i / (D/32), d block
+      // i % (D/32)): consecutive MFMAs update different accumulators; the
+      // transposed V operand reads run TILEATTN_PREFETCH MFMAs ahead.
       if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+      {
+        typedef short i16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        constexpr int kN = 4 * (D / 32);
+        constexpr int kP = TILEATTN_PREFETCH;
+        bf16x8 ring[kP];
+        auto fetch = [&](int i) {
+          const int g = i / (D / 32), db = i % (D / 32);
+          const int o0 = 16 * g * T::kVPitch + db * 64;  // g = kb*2 + t
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vs + o0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(uintptr_t)(vs + o0 + 8 * T::kVPitch));
+          ring[i % kP] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int i = 0; i < kP; ++i) fetch(i);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            typedef short i16x4 __attribute__((ext_vector_type(4)));
-            typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-            const int o0 = (kb * 32 + 16 * t) * T::kVPitch + db * 64;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(uintptr_t)(vs + o0));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(uintptr_t)(vs + o0 + 8 * T::kVPitch));
-            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][t], acc[db], 0, 0, 0);
-          }
+        for (int i = 0; i < kN; ++i) {
+          const int g = i / (D / 32), db = i % (D / 32);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kP], pf[g >> 1][g & 1], acc[db], 0, 0, 0);
+          if (i + kP < kN) fetch(i + kP);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
     }
 
