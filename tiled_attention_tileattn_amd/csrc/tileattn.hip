@@ -15,8 +15,9 @@
 // Troubleshooting note on fp16 accumulators).
 //
 // CDNA4 mapping (our design, not the pages'):
-//   * One workgroup = 4 waves = 128 query rows of one (batch, query head);
-//     each wave owns 32 query rows for the whole key loop.
+//   * One workgroup = 8 waves = 256 query rows of one (batch, query head);
+//     each wave owns 32 query rows for the whole key loop.  Two waves share
+//     each SIMD (wave w and w+4).
 //   * The kernel computes the transposed products S^T = K * Q^T and
 //     O^T = V^T * P^T with v_mfma_f32_32x32x16_bf16.  In the 32x32 result
 //     layout a lane holds 16 entries of ONE output column, so with queries as
@@ -24,17 +25,24 @@
 //     in-lane reductions plus one v_permlane32_swap between the two lanes
 //     that share the row, and the rescale factor is a per-lane scalar.
 //   * The fp32 S^T tile, once exponentiated and packed to bf16, is already
-//     in the B-operand layout of the P*V product (no LDS round trip); V is
-//     stored transposed in LDS with the key order permuted to match it.
+//     in the B-operand layout of the P*V product (no LDS round trip); the V
+//     operand is read from row-major LDS with ds_read_b64_tr_b16, whose
+//     transpose yields exactly the key order that P^T carries.
 //   * Q lives in VGPRs for the whole loop (B operand of the first product).
-//   * K and V^T tiles are double-buffered in LDS; the next tile's global
-//     loads are issued before the current tile's math and written to the
-//     other buffer after it.  K rows are XOR-swizzled in 16-byte chunks so
-//     the 32 rows one MFMA operand read touches fall in distinct banks.
-//   * exp is computed as exp2 with scale*log2(e) folded into one FMA.
-//   * Causal: tiles entirely above the diagonal are never loaded; a wave whose
-//     rows see no key of a tile skips its math; masking code runs only on the
-//     diagonal tile(s) and the ragged last key tile.
+//   * K and V tiles are double-buffered in LDS with padded row pitches (no
+//     bank conflicts); operands are read into a small register ring a few
+//     MFMAs ahead of use.
+//   * Ping-pong: the waves of a SIMD alternate between a matrix phase (only
+//     MFMAs: the scores of tile j and the P*V update of tile j-1) and a
+//     vector phase (the online softmax), half a tile apart, so that one wave
+//     keeps the matrix core busy while the other exponentiates.
+//   * exp is computed as exp2 with scale*log2(e) folded into one FMA; the
+//     reference max is raised lazily (see softmax_tile), which is exact.
+//   * Causal: tiles entirely above a workgroup's diagonal are never loaded;
+//     masking code runs only on tiles that cross a wave's diagonal or the
+//     ragged end.  A wave whose rows end before the workgroup's last tile
+//     runs the remaining tiles fully masked (p = 0), which keeps both wave
+//     groups in step with the shared barriers.
 //   * Workgroup ids are remapped so the workgroups that one XCD (8 per chip,
 //     ids dealt round-robin) runs share a key/value head and read its K/V
 //     tiles from that XCD's L2; causal query tiles go heaviest first.
@@ -42,6 +50,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
+#include <type_traits>
 
 #include "../../include/tileattn.h"
 
@@ -72,39 +81,6 @@ __device__ __forceinline__ float wave_pair_max(float x) {
 __device__ __forceinline__ float wave_pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Steps (2)-(3) of the tile update for one lane's 32 scores of its query row:
-// raise the running max, return the rescale factor alpha = exp(old - new)
-// (scaled units), overwrite the scores with p = exp2(s*c - m*c) and fold
-// their sum into the lane's running sum.  MASKED tiles carry -inf scores,
-// which must give p = 0 even when c = 0.
-template <bool MASKED>
-__device__ __forceinline__ float online_softmax_step(f32x16 (&s)[2], float& m_run, float& l_run,
-                                                     float c) {
-  float mx = s[0][0];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = wave_pair_max(mx);
-  const float m_new = fmaxf(m_run, mx);
-  const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
-  m_run = m_new;
-  const float mc = m_new * c;
-  float psum = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float x = s[kb][r];
-      float p = __builtin_amdgcn_exp2f(fmaf(x, c, -mc));
-      if (MASKED) p = (x == -INFINITY) ? 0.f : p;
-      s[kb][r] = p;
-      psum += p;
-    }
-  l_run = l_run * alpha + psum;
-  return alpha;
 }
 
 // Map a hardware workgroup id to (batch, query head, query tile).  Ids are
@@ -144,10 +120,6 @@ __device__ __forceinline__ void map_workgroup(int hw_id, int nwg, int Hkv, int G
 #ifndef TILEATTN_PREFETCH
 #define TILEATTN_PREFETCH 4
 #endif
-// 1: global->register tile loads clamp the row index (no branches).
-#ifndef TILEATTN_CLAMPED_LOADS
-#define TILEATTN_CLAMPED_LOADS 1
-#endif
 
 template <int D>
 struct Bf16Tile {
@@ -166,7 +138,6 @@ struct Bf16Tile {
   static constexpr int kVPitch = D * 2 + 64;
   static constexpr int kKBytes = kBlockN * kKPitch;
   static constexpr int kVBytes = kBlockN * kVPitch;
-  static constexpr int kStageBytes = kKBytes + kVBytes;    // K tile then V tile
   static constexpr int kLoads = kBlockN * kChunks / kThreads;  // 16-byte loads per tensor
   static_assert(kLoads >= 1 && kLoads * kThreads == kBlockN * kChunks, "tile/threads mismatch");
 };
@@ -179,9 +150,9 @@ struct Bf16Tile {
 // overflow.  When the branch is taken every lane rescales its accumulator and
 // running sum by alpha = exp2((m_old - m_new) * c).  The running sum adds the
 // fp32 p; p is then packed to bf16 (round to nearest even) in the B-operand
-// layout of the P*V product.  MASKED tiles carry -inf scores, which must give
-// p = 0 even when c = 0.
-template <bool MASKED, int NACC>
+// layout of the P*V product.  Masked scores are -inf; with c > 0 they give
+// p = exp2(-inf) = 0.
+template <int NACC>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& m_run, float& l_run,
                                              float c, f32x16 (&acc)[NACC],
                                              bf16x8 (&pf)[2][2]) {
@@ -208,13 +179,8 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& m_run, float
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const float x0 = s[kb][8 * t + e], x1 = s[kb][8 * t + e + 1];
-        float p0 = __builtin_amdgcn_exp2f(fmaf(x0, c, -mc));
-        float p1 = __builtin_amdgcn_exp2f(fmaf(x1, c, -mc));
-        if (MASKED) {
-          p0 = (x0 == -INFINITY) ? 0.f : p0;
-          p1 = (x1 == -INFINITY) ? 0.f : p1;
-        }
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * t + e], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * t + e + 1], c, -mc));
         psum0 += p0;
         psum1 += p1;
         pf[kb][t][e] = (__bf16)p0;
@@ -223,41 +189,48 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& m_run, float
   l_run += psum0 + psum1;
 }
 
+// Ping-pong schedule.  The 8 waves form two groups (waves 0-3 and 4-7, one
+// wave of each on every SIMD).  Per 64-key tile j a wave runs a matrix phase
+// M(j) (MFMAs only: S_j = K_j Q^T interleaved with acc += V_{j-1}^T P_{j-1}^T)
+// and a vector phase V(j) (the online softmax of S_j into P_j).  Group 0 runs
+// M(j) then V(j) in the two halves of iteration j; group 1 runs V(j-1) then
+// M(j).  A barrier separates the halves, so on every SIMD one wave drives the
+// matrix core while the other works through its exponentials.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* K,
     const uint16_t* V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Hq, int Hkv, int Sq, int Sk, float scale, int nqt, int nwg) {
   using T = Bf16Tile<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::kStageBytes];
+  static_assert(T::kWaves == 8, "two groups of four waves");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::kKBytes + 2 * T::kVBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int half = lane >> 5;  // which 32-lane half
+  const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int group = wave >> 2;
   const int G = Hq / Hkv;
 
   int b, hq, qt;
   map_workgroup(blockIdx.x, nwg, Hkv, G, nqt, CAUSAL, b, hq, qt);
   const int hk = hq / G;
   const int q0 = qt * T::kBlockM;
-  const int qw = q0 + wave * kRowsPerWave;  // first query row of this wave
-  const int my_row = qw + l32;              // query row owned by this lane
+  const int qw = q0 + wave * kRowsPerWave;
+  const int my_row = qw + l32;
 
   const size_t q_head = ((size_t)b * Hq + hq) * (size_t)Sq;
   const size_t kv_head = ((size_t)b * Hkv + hk) * (size_t)Sk;
   const uint16_t* Kh = K + kv_head * D;
   const uint16_t* Vh = V + kv_head * D;
 
-  // Key tiles this workgroup visits (causal: up to its last valid row).
   int nkt = (Sk + kBlockN - 1) / kBlockN;
   if (CAUSAL) {
     const int last_row = min(q0 + T::kBlockM - 1, Sq - 1);
     nkt = min(nkt, last_row / kBlockN + 1);
   }
 
-  // ---- Q fragment: B operand of S^T = K Q^T (k = d, n = query) ------------
   bf16x8 qf[D / 16];
   {
     const bool ok = my_row < Sq;
@@ -270,157 +243,144 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
     }
   }
 
-  // ---- tile loaders: global -> registers -> LDS (row-major, swizzled) -----
+  // ---- tile loaders: global -> registers -> LDS ---------------------------
   u32x4 kreg[T::kLoads], vreg[T::kLoads];
-  auto load_tile = [&](int j) {
+  auto load_rows = [&](const uint16_t* base, int j, u32x4 (&reg)[T::kLoads]) {
     const int key0 = j * kBlockN;
 #pragma unroll
     for (int i = 0; i < T::kLoads; ++i) {
       const int idx = tid + i * T::kThreads;
-      const int r = idx / T::kChunks, cc = idx % T::kChunks;  // coalesced along a row
-      if (TILEATTN_CLAMPED_LOADS) {
-        // Rows past the last key are clamped to it: those keys are masked to
-        // p = 0 and the clamped rows hold finite input data.
-        const size_t g = (size_t)min(key0 + r, Sk - 1) * D + cc * 8;
-        kreg[i] = *reinterpret_cast<const u32x4*>(Kh + g);
-        vreg[i] = *reinterpret_cast<const u32x4*>(Vh + g);
-      } else {
-        const bool ok = key0 + r < Sk;
-        const size_t g = (size_t)(key0 + r) * D + cc * 8;
-        kreg[i] = ok ? *reinterpret_cast<const u32x4*>(Kh + g) : u32x4{0, 0, 0, 0};
-        vreg[i] = ok ? *reinterpret_cast<const u32x4*>(Vh + g) : u32x4{0, 0, 0, 0};
-      }
+      const int r = idx / T::kChunks, cc = idx % T::kChunks;
+      // Rows past the last key are clamped to it: those keys are masked.
+      const size_t g = (size_t)min(key0 + r, Sk - 1) * D + cc * 8;
+      reg[i] = *reinterpret_cast<const u32x4*>(base + g);
     }
   };
-  auto store_tile = [&](int stage) {
-    unsigned char* ks = smem + stage * T::kStageBytes;
-    unsigned char* vs = ks + T::kKBytes;
+  auto store_rows = [&](int byte0, int pitch, const u32x4 (&reg)[T::kLoads]) {
 #pragma unroll
     for (int i = 0; i < T::kLoads; ++i) {
       const int idx = tid + i * T::kThreads;
       const int r = idx / T::kChunks, cc = idx % T::kChunks;
-      *reinterpret_cast<u32x4*>(ks + r * T::kKPitch + cc * 16) = kreg[i];
-      *reinterpret_cast<u32x4*>(vs + r * T::kVPitch + cc * 16) = vreg[i];
+      *reinterpret_cast<u32x4*>(smem + byte0 + r * pitch + cc * 16) = reg[i];
     }
   };
+  auto kslot = [](int j) { return (j & 1) * T::kKBytes; };
+  auto vslot = [](int j) { return 2 * T::kKBytes + (j & 1) * T::kVBytes; };
 
-  // Per-lane byte offsets of the operand reads (tile-independent).
-  // K (A operand of S^T): row kb*32 + l32, bytes 32*kk + 16*half.
-  // V (A operand of O^T, read transposed with ds_read_b64_tr_b16): in each
-  // 16-lane group, source lane s reads 4 consecutive d of key row
-  // (s >> 2); output lane 4a+b then holds d = 4a+b of 4 consecutive keys.
-  // The key rows of one read are kb*32 + 16t + 8rd + 4*half + (s >> 2), so
-  // lanes 0-31 receive keys {0-3, 8-11} and lanes 32-63 keys {4-7, 12-15} of
-  // each 16-key step: exactly the k order of the P^T operand built from the
-  // S^T accumulator layout.
   const int s16 = lane & 15;
   const int k_lane_off = l32 * T::kKPitch + 16 * half;
   const int v_lane_off = (4 * half + (s16 >> 2)) * T::kVPitch +
                          2 * (16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
 
-  // ---- running state (per lane: one query row, half of its keys) ----------
+  auto k_operand = [&](int kbase, int i) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(smem + kbase + (i & 1) * 32 * T::kKPitch + (i >> 1) * 32);
+  };
+  auto v_operand = [&](int vbase, int i) -> bf16x8 {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const int g = i / (D / 32), db = i % (D / 32);
+    const unsigned char* vs = smem + vbase + 16 * g * T::kVPitch + db * 64;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)vs);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vs + 8 * T::kVPitch));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
-  float m_run = -INFINITY;  // reference max of raw scores q.k
-  float l_run = 0.f;        // this lane's partial running sum
-  const float c = scale * kLog2e;
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+  bf16x8 pf[2][2];
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  // exp2 argument scale, scale*log2(e), kept >= the smallest normal float: a
+  // zero (or tiny) scale then still gives every visible key p = exp2(~0) = 1
+  // exactly, as scale = 0 does, while masked -inf scores keep p = 0.
+  const float c = fmaxf(scale * kLog2e, 1.17549435e-38f);
 
-  load_tile(0);
-  store_tile(0);
+  constexpr int kN = 2 * (D / 16);  // MFMAs of each product per tile
+  static_assert(kN == 4 * (D / 32), "both products take the same number of MFMAs");
+  constexpr int kP = TILEATTN_PREFETCH;
+
+  // Matrix phase: S_j (WITH_S) and acc += V_{j-1}^T P_{j-1}^T (WITH_PV),
+  // MFMA by MFMA alternating, operands read kP steps ahead.
+  auto matrix_phase = [&](auto with_s_c, auto with_pv_c, int j) {
+    constexpr bool WITH_S = decltype(with_s_c)::value;
+    constexpr bool WITH_PV = decltype(with_pv_c)::value;
+    const int kb = kslot(j) + k_lane_off, vb = vslot(j - 1) + v_lane_off;
+    if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+    bf16x8 kring[kP], vring[kP];
+#pragma unroll
+    for (int i = 0; i < kP; ++i) {
+      if (WITH_S) kring[i] = k_operand(kb, i);
+      if (WITH_PV) vring[i] = v_operand(vb, i);
+    }
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      if (WITH_S)
+        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kring[i % kP], qf[i >> 1],
+                                                          i < 2 ? f32x16{} : s[i & 1], 0, 0, 0);
+      if (WITH_PV) {
+        const int g = i / (D / 32), db = i % (D / 32);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vring[i % kP], pf[g >> 1][g & 1], acc[db], 0, 0, 0);
+      }
+      if (i + kP < kN) {
+        if (WITH_S) kring[i % kP] = k_operand(kb, i + kP);
+        if (WITH_PV) vring[i % kP] = v_operand(vb, i + kP);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Vector phase: mask tile j where needed, online softmax, pack P_j.
+  // Tiles past a causal wave's diagonal come out fully masked (p = 0): the
+  // tile max is -inf, the reference max stays, and acc and l are unchanged.
+  auto vector_phase = [&](int j) {
+    const int key0 = j * kBlockN;
+    const bool need_mask = (CAUSAL && key0 + kBlockN - 1 > qw) || (key0 + kBlockN > Sk);
+    if (need_mask) {
+      const int lim = (CAUSAL ? min(Sk - 1, my_row) : Sk - 1) - key0 - 4 * half;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) <= lim) ? s[kb][r] : -INFINITY;
+    }
+    // c > 0 here, so a masked (-inf) score gives p = exp2(-inf) = 0 without
+    // a separate masked code path.
+    softmax_tile(s, m_run, l_run, c, acc, pf);
+  };
+
+  using TT = std::true_type;
+  using FF = std::false_type;
+  // One iteration: loads of K_{j+1} and V_j at the top, the two halves, the
+  // stores into the slots no wave reads in this iteration, the closing barrier.
+  auto iteration = [&](int j, auto first, auto second) {
+    const bool ld_k = j + 1 < nkt, ld_v = j < nkt;
+    if (ld_k) load_rows(Kh, j + 1, kreg);
+    if (ld_v) load_rows(Vh, j, vreg);
+    first();
+    __builtin_amdgcn_s_barrier();
+    second();
+    if (ld_k) store_rows(kslot(j + 1), T::kKPitch, kreg);
+    if (ld_v) store_rows(vslot(j), T::kVPitch, vreg);
+    __syncthreads();
+  };
+
+  load_rows(Kh, 0, kreg);
+  store_rows(kslot(0), T::kKPitch, kreg);
   __syncthreads();
 
-  for (int j = 0; j < nkt; ++j) {
-    const int stage = j & 1;
-    const bool has_next = (j + 1) < nkt;
-    if (has_next) load_tile(j + 1);
-
-    const int key0 = j * kBlockN;
-    const bool wave_active = !CAUSAL || key0 <= qw + kRowsPerWave - 1;
-    if (wave_active) {
-      const unsigned char* ks = smem + stage * T::kStageBytes + k_lane_off;
-      const unsigned char* vs = smem + stage * T::kStageBytes + T::kKBytes + v_lane_off;
-
-      // (1) S^T = K Q^T: two 32-key blocks, fp32 accumulation.  MFMA i uses
-      // K operand i (kk = i/2, block i%2); operands are read from LDS
-      // TILEATTN_PREFETCH MFMAs ahead into a register ring, and each step is
-      // fenced so the scheduler cannot pull the reads back next to their use.
-      if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-      {
-        constexpr int kN = 2 * (D / 16);
-        constexpr int kP = TILEATTN_PREFETCH;
-        bf16x8 ring[kP];
-        auto fetch = [&](int i) {
-          ring[i % kP] = *reinterpret_cast<const bf16x8*>(ks + (i & 1) * 32 * T::kKPitch + (i >> 1) * 32);
-        };
-#pragma unroll
-        for (int i = 0; i < kP; ++i) fetch(i);
-#pragma unroll
-        for (int i = 0; i < kN; ++i) {
-          s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kP], qf[i >> 1], s[i & 1], 0, 0, 0);
-          if (i + kP < kN) fetch(i + kP);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-
-      // (2)-(4a) mask (diagonal / ragged tiles only), online softmax, pack P.
-      bf16x8 pf[2][2];
-      const bool need_mask = (CAUSAL && key0 + kBlockN - 1 > qw) || (key0 + kBlockN > Sk);
-      if (need_mask) {
-        // Entry r of block kb is key key0 + kb*32 + 8*(r>>2) + 4*half + (r&3);
-        // it is visible iff that key <= min(Sk - 1, my_row) (causal) or
-        // <= Sk - 1: one per-lane limit against compile-time offsets.
-        const int lim = (CAUSAL ? min(Sk - 1, my_row) : Sk - 1) - key0 - 4 * half;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) <= lim) ? s[kb][r] : -INFINITY;
-        softmax_tile<true>(s, m_run, l_run, c, acc, pf);
-      } else {
-        softmax_tile<false>(s, m_run, l_run, c, acc, pf);
-      }
-
-      // Without the causal branch around the tile body the scheduler
-      // overlaps the softmax with the P*V operand reads far enough to spill;
-      // a fence between the two keeps the live ranges apart.
-      if constexpr (!CAUSAL) __builtin_amdgcn_sched_barrier(0);
-
-      // (4b) acc += V^T P^T.  MFMA i = (16-key group g = i / (D/32), d block
-      // i % (D/32)): consecutive MFMAs update different accumulators; the
-      // transposed V operand reads run TILEATTN_PREFETCH MFMAs ahead.
-      if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-      {
-        typedef short i16x4 __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-        constexpr int kN = 4 * (D / 32);
-        constexpr int kP = TILEATTN_PREFETCH;
-        bf16x8 ring[kP];
-        auto fetch = [&](int i) {
-          const int g = i / (D / 32), db = i % (D / 32);
-          const int o0 = 16 * g * T::kVPitch + db * 64;  // g = kb*2 + t
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vs + o0));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(uintptr_t)(vs + o0 + 8 * T::kVPitch));
-          ring[i % kP] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-#pragma unroll
-        for (int i = 0; i < kP; ++i) fetch(i);
-#pragma unroll
-        for (int i = 0; i < kN; ++i) {
-          const int g = i / (D / 32), db = i % (D / 32);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kP], pf[g >> 1][g & 1], acc[db], 0, 0, 0);
-          if (i + kP < kN) fetch(i + kP);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-    }
-
-    if (has_next) store_tile(stage ^ 1);
-    __syncthreads();
+  if (group == 0) {
+    iteration(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
+    for (int j = 1; j < nkt; ++j)
+      iteration(j, [&] { matrix_phase(TT{}, TT{}, j); }, [&] { vector_phase(j); });
+    iteration(nkt, [&] { matrix_phase(FF{}, TT{}, nkt); }, [&] {});
+  } else {
+    iteration(0, [&] {}, [&] { matrix_phase(TT{}, FF{}, 0); });
+    for (int j = 1; j < nkt; ++j)
+      iteration(j, [&] { vector_phase(j - 1); }, [&] { matrix_phase(TT{}, TT{}, j); });
+    iteration(nkt, [&] { vector_phase(nkt - 1); }, [&] { matrix_phase(FF{}, TT{}, nkt); });
   }
 
   // ---- epilogue: O = acc / l, lse = m*scale + ln l --------------------------

@@ -67,6 +67,8 @@ def main():
     ap.add_argument("--flop", type=float, default=549755813888.0)
     ap.add_argument("--compulsory-bytes", type=float, default=168820736.0)
     ap.add_argument("--commands", nargs="*", default=[])
+    ap.add_argument("--bench-log", default=None,
+                    help="stdout of the profiled bench.py run (its JSON line)")
     a = ap.parse_args()
 
     tr = trace_stats(a.trace, KERNEL_KEY)
@@ -82,6 +84,11 @@ def main():
     fetch_b = fetch_kib * 1024.0 * f_scale
     write_b = write_kib * 1024.0 * w_scale
     avg_s = tr["avg_ns"] * 1e-9
+    bench = None
+    if a.bench_log:
+        for line in open(a.bench_log):
+            if line.startswith("{"):
+                bench = json.loads(line)
     gui = sq.get("GRBM_GUI_ACTIVE", float("nan"))
     xcds = 8
     simds = 1024
@@ -106,6 +113,7 @@ def main():
         "valu_insts": sq.get("SQ_INSTS_VALU"),
         "mfma_insts": sq.get("SQ_INSTS_MFMA"),
         "lds_insts": sq.get("SQ_INSTS_LDS"),
+        "bench_event_mean_ns": (a.flop / (bench["roofline"]["achieved"] * 1e12) * 1e9) if bench else None,
     }
     lines = [
         f"# rocprofv3: {KERNEL_KEY}, {a.workload}",
@@ -118,6 +126,8 @@ def main():
         f"| dispatches profiled | {tr['calls']} |",
         f"| average kernel time | {tr['avg_ns']/1e3:.1f} us (min {tr['min_ns']/1e3:.1f}, max {tr['max_ns']/1e3:.1f}) |",
         f"| TFLOP/s at the average (counted FLOP {a.flop:.4g}) | {fig['tflops_at_avg']:.1f} |",
+        (f"| bench.py's own HIP-event mean in the traced run | {fig['bench_event_mean_ns']/1e3:.1f} us "
+         f"(roofline.achieved {bench['roofline']['achieved']:.1f} TFLOP/s) |") if bench else "| bench.py line | not recorded |",
         f"| HBM fetch (FETCH_SIZE x {f_scale:.3f}) | {fetch_b/2**20:.1f} MiB |",
         f"| HBM write (WRITE_SIZE x {w_scale:.3f}) | {write_b/2**20:.1f} MiB |",
         f"| compulsory bytes (Q, K, V read; O, lse written) | {a.compulsory_bytes/2**20:.1f} MiB |",
