@@ -56,7 +56,9 @@ typedef enum {
   TILEATTN_ERR_HEAD_DIM = -4,     /* D is not 64 or 128                               */
   TILEATTN_ERR_SCALE = -5,        /* scale is negative, NaN or infinite               */
   TILEATTN_ERR_ALIGNMENT = -6,    /* a pointer is not 16-byte aligned                 */
-  TILEATTN_ERR_TOO_LARGE = -7,    /* a size product exceeds the 64-bit index range    */
+  TILEATTN_ERR_TOO_LARGE = -7,    /* a size product exceeds the 64-bit index range,   */
+                                  /* or Sk*D*4 > 2^31-1 (one head's K or V is read    */
+                                  /* with 32-bit buffer offsets)                      */
   TILEATTN_ERR_LAUNCH = -8        /* the HIP launch failed (e.g. no gfx950 device)    */
 } tileattn_status;
 

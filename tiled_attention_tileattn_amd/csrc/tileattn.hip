@@ -71,6 +71,9 @@ constexpr int kF32Threads = kF32Waves * 64;
 constexpr int kF32BlockM = kF32Waves * kRowsPerWave;   // fp32 path: 128 query rows
 constexpr int kBlockNF32 = 32;                         // keys per tile (fp32 path)
 constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format,
+// no swizzle, no stride): loads past num_records return 0.
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ float wave_pair_max(float x) {
   // Lanes l and l^32 hold the same query row; combine their partial maxima.
@@ -244,16 +247,20 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
   }
 
   // ---- tile loaders: global -> registers -> LDS ---------------------------
+  // Buffer loads over this head's K and V: the tile offset is a scalar, the
+  // per-thread offset a constant, and rows past Sk fall outside the buffer
+  // range and read as 0 (those keys are masked).
+  const int kv_bytes = Sk * D * 2;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, 0, kv_bytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, 0, kv_bytes, kBufferFlags);
   u32x4 kreg[T::kLoads], vreg[T::kLoads];
-  auto load_rows = [&](const uint16_t* base, int j, u32x4 (&reg)[T::kLoads]) {
-    const int key0 = j * kBlockN;
+  auto load_rows = [&](const __amdgpu_buffer_rsrc_t& rsrc, int j, u32x4 (&reg)[T::kLoads]) {
+    const int tile_off = j * kBlockN * D * 2;
 #pragma unroll
     for (int i = 0; i < T::kLoads; ++i) {
       const int idx = tid + i * T::kThreads;
       const int r = idx / T::kChunks, cc = idx % T::kChunks;
-      // Rows past the last key are clamped to it: those keys are masked.
-      const size_t g = (size_t)min(key0 + r, Sk - 1) * D + cc * 8;
-      reg[i] = *reinterpret_cast<const u32x4*>(base + g);
+      reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (r * D + cc * 8) * 2, tile_off, 0));
     }
   };
   auto store_rows = [&](int byte0, int pitch, const u32x4 (&reg)[T::kLoads]) {
@@ -357,8 +364,8 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
   // stores into the slots no wave reads in this iteration, the closing barrier.
   auto iteration = [&](int j, auto first, auto second) {
     const bool ld_k = j + 1 < nkt, ld_v = j < nkt;
-    if (ld_k) load_rows(Kh, j + 1, kreg);
-    if (ld_v) load_rows(Vh, j, vreg);
+    if (ld_k) load_rows(krsrc, j + 1, kreg);
+    if (ld_v) load_rows(vrsrc, j, vreg);
     first();
     __builtin_amdgcn_s_barrier();
     second();
@@ -367,7 +374,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
     __syncthreads();
   };
 
-  load_rows(Kh, 0, kreg);
+  load_rows(krsrc, 0, kreg);
   store_rows(kslot(0), T::kKPitch, kreg);
   __syncthreads();
 
@@ -559,7 +566,10 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
   const double q_elems = (double)B * Hq * Sq * D;
   const double kv_elems = (double)B * Hkv * Sk * D;
   const double nwg = (double)B * Hq * ((Sq + kF32BlockM - 1) / kF32BlockM);  // smallest block_m
-  if (q_elems > 9.0e18 || kv_elems > 9.0e18 || nwg > 2147483647.0) return TILEATTN_ERR_TOO_LARGE;
+  // One head's K or V is addressed with 32-bit buffer offsets.
+  const double head_bytes = (double)Sk * D * 4;
+  if (q_elems > 9.0e18 || kv_elems > 9.0e18 || nwg > 2147483647.0 || head_bytes > 2147483647.0)
+    return TILEATTN_ERR_TOO_LARGE;
   if (B == 0 || Hq == 0 || Sq == 0) {
     *empty = true;
     return TILEATTN_OK;
