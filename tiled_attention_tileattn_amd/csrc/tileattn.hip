@@ -362,7 +362,15 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
   using FF = std::false_type;
   // One iteration: loads of K_{j+1} and V_j at the top, the two halves, the
   // stores into the slots no wave reads in this iteration, the closing barrier.
-  auto iteration = [&](int j, auto first, auto second) {
+  // Each group stages its own half of every tile's rows (thread tid covers
+  // chunks tid and tid + 512), and writes it to LDS while the other group runs
+  // its matrix phase, off the critical path:
+  //   group 0, iteration j: load K_{j+1}, V_j | M(j) | V(j), store them;
+  //   group 1, iteration j: store K_{j+1}, V_j (loaded one iteration
+  //     earlier), load K_{j+2}, V_{j+1} | V(j-1) | M(j).
+  // Both write the slots that K_{j-1} and V_{j-2} left; the closing barrier
+  // publishes the whole tile for iteration j+1.
+  auto iteration0 = [&](int j, auto first, auto second) {
     const bool ld_k = j + 1 < nkt, ld_v = j < nkt;
     if (ld_k) load_rows(krsrc, j + 1, kreg);
     if (ld_v) load_rows(vrsrc, j, vreg);
@@ -373,21 +381,35 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
     if (ld_v) store_rows(vslot(j), T::kVPitch, vreg);
     __syncthreads();
   };
+  auto iteration1 = [&](int j, auto first, auto second) {
+    if (j + 1 < nkt) store_rows(kslot(j + 1), T::kKPitch, kreg);
+    if (j < nkt) store_rows(vslot(j), T::kVPitch, vreg);
+    if (j + 2 < nkt) load_rows(krsrc, j + 2, kreg);
+    if (j + 1 < nkt) load_rows(vrsrc, j + 1, vreg);
+    first();
+    __builtin_amdgcn_s_barrier();
+    second();
+    __syncthreads();
+  };
 
   load_rows(krsrc, 0, kreg);
   store_rows(kslot(0), T::kKPitch, kreg);
+  if (group == 1) {
+    if (nkt > 1) load_rows(krsrc, 1, kreg);
+    load_rows(vrsrc, 0, vreg);
+  }
   __syncthreads();
 
   if (group == 0) {
-    iteration(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
+    iteration0(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
     for (int j = 1; j < nkt; ++j)
-      iteration(j, [&] { matrix_phase(TT{}, TT{}, j); }, [&] { vector_phase(j); });
-    iteration(nkt, [&] { matrix_phase(FF{}, TT{}, nkt); }, [&] {});
+      iteration0(j, [&] { matrix_phase(TT{}, TT{}, j); }, [&] { vector_phase(j); });
+    iteration0(nkt, [&] { matrix_phase(FF{}, TT{}, nkt); }, [&] {});
   } else {
-    iteration(0, [&] {}, [&] { matrix_phase(TT{}, FF{}, 0); });
+    iteration1(0, [&] {}, [&] { matrix_phase(TT{}, FF{}, 0); });
     for (int j = 1; j < nkt; ++j)
-      iteration(j, [&] { vector_phase(j - 1); }, [&] { matrix_phase(TT{}, TT{}, j); });
-    iteration(nkt, [&] { vector_phase(nkt - 1); }, [&] { matrix_phase(FF{}, TT{}, nkt); });
+      iteration1(j, [&] { vector_phase(j - 1); }, [&] { matrix_phase(TT{}, TT{}, j); });
+    iteration1(nkt, [&] { vector_phase(nkt - 1); }, [&] { matrix_phase(FF{}, TT{}, nkt); });
   }
 
   // ---- epilogue: O = acc / l, lse = m*scale + ln l --------------------------
