@@ -78,6 +78,20 @@ int tileattn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  float scale, int causal, void* stream);
 
 /*
+ * float16 attention forward: the same contract as tileattn_fwd with fp16
+ * (IEEE binary16) q, k, v and o.  The first page's own kernel is written for
+ * fp16 inputs with fp32 accumulation, casting the probabilities to the value
+ * dtype before the second product (Passo a Passo, step 6, and its
+ * Troubleshooting note on fp16 accumulators); this entry point runs that
+ * dtype on the same kernel with fp16 matrix-core instructions.  The
+ * probabilities are rounded to fp16 (nearest even); they never exceed 2^8,
+ * far inside fp16 range, and o stays within the range of v.
+ */
+int tileattn_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                     float scale, int causal, void* stream);
+
+/*
  * float32 attention forward: the same contract as tileattn_fwd with fp32
  * q, k, v and o.  Both products use fp32 matrix-core instructions and the
  * probabilities stay fp32 (there is no narrower value dtype to cast them to).
@@ -93,7 +107,7 @@ const char* tileattn_strerror(int status);
  * Launch geometry the library uses for a problem: query rows per workgroup
  * (block_m), keys per tile (block_n) and the number of workgroups.  For
  * reporting and tests; pure host arithmetic, no HIP call.  dtype_bytes is 2
- * (bf16) or 4 (fp32).  Returns TILEATTN_OK or the error tileattn_fwd would.
+ * (bf16 or fp16) or 4 (fp32).  Returns TILEATTN_OK or the error tileattn_fwd would.
  */
 int tileattn_launch_shape(int dtype_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D,
                           int causal, int* block_m, int* block_n, long long* workgroups);

@@ -306,6 +306,20 @@ def test_inputs_are_deterministic_and_follow_the_recipe():
     assert qb.dtype == torch.bfloat16
     g = torch.Generator("cpu").manual_seed(1)
     assert torch.equal(qb, torch.randn(4, 8, 16, 64, generator=g).to(torch.bfloat16))
+    wh = WORKLOADS["causal_gqa_fp16"].with_(Sq=16, Sk=16)
+    qh, kh, vh = make_inputs(wh)
+    assert qh.dtype == kh.dtype == vh.dtype == torch.float16
+    g = torch.Generator("cpu").manual_seed(5)
+    assert torch.equal(qh, torch.randn(1, 32, 16, 128, generator=g).to(torch.float16))
+
+
+def test_oracle_takes_fp16_values_exactly():
+    # fp16 inputs reach the oracle as their exact binary16 values, and the
+    # result is the same as for those values given in float64.
+    q, k, v = random_qkv(1, 2, 1, 9, 11, 16, dtype="fp16", seed=51)
+    o16, l16 = oracle.attention(q, k, v, 0.25, True)
+    o64, l64 = oracle.attention(q.double(), k.double(), v.double(), 0.25, True)
+    assert np.array_equal(o16, o64) and np.array_equal(l16, l64)
 
 
 def test_long_context_sample_is_reproducible():

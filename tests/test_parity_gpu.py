@@ -6,9 +6,13 @@ element by element with ``oracle`` on the same input values.
 
 Tolerances (on O, over all compared elements):
     bf16 inputs: max |err| <= 2e-2 and mean |err| <= 2e-3
+    fp16 inputs: max |err| <= 4e-3 and mean |err| <= 4e-4
     fp32 inputs: max |err| <= 1e-4
+The fp16 bound scales the bf16 one by the ratio of the two formats' unit
+roundoffs (2^-11 / 2^-8 = 1/8) and rounds up: the error is dominated by the
+rounding of P and of O to the 16-bit dtype.
 On lse (not specified elsewhere; derived from the arithmetic: fp32 sums of
-exact products and the hardware exp2/log): <= 1e-3 (bf16), <= 1e-4 (fp32).
+exact products and the hardware exp2/log): <= 1e-3 (bf16, fp16), <= 1e-4 (fp32).
 """
 
 import math
@@ -24,7 +28,8 @@ from tiled_attention_tileattn_amd.inputs import WORKLOADS, make_inputs, random_q
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": dict(max=2e-2, mean=2e-3, lse=1e-3), "fp32": dict(max=1e-4, mean=1e-4, lse=1e-4)}
+TOL = {"bf16": dict(max=2e-2, mean=2e-3, lse=1e-3), "fp16": dict(max=4e-3, mean=4e-4, lse=1e-3),
+       "fp32": dict(max=1e-4, mean=1e-4, lse=1e-4)}
 
 
 def _say(msg):
@@ -97,12 +102,18 @@ def test_sweep_bf16(shape, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SWEEP[1::2])
+def test_sweep_fp16(shape, causal):
+    _parity(*shape, causal=causal, dtype="fp16", seed=3 + sum(shape))
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SWEEP[::2])
 def test_sweep_fp32(shape, causal):
     _parity(*shape, causal=causal, dtype="fp32", seed=7 + sum(shape))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 def test_scale_edge_values(dtype):
     # scale = 0: every visible key weighs the same; large scale: peaky softmax.
     _parity(1, 4, 2, 150, 150, 128, True, dtype, seed=3, scale=0.0)
@@ -190,7 +201,7 @@ def test_empty_query_set_is_a_noop():
 
 
 # ---------------------------------------------------------------------------
-# The five workloads at full size.
+# The workloads at full size.
 # ---------------------------------------------------------------------------
 def _edge_rows(w, n_extra, seed):
     """Flat row indices: first/last rows of heads, tile boundaries, plus random."""
@@ -215,7 +226,8 @@ def test_workload_full_oracle(name):
     _check(o, lse, o_ref, lse_ref, w.dtype, name)
 
 
-@pytest.mark.parametrize("name", ["causal_mha_bf16", "causal_gqa_bf16", "longctx_gqa_bf16"])
+@pytest.mark.parametrize("name", ["causal_mha_bf16", "causal_gqa_bf16", "longctx_gqa_bf16",
+                                  "causal_gqa_fp16"])
 def test_workload_sampled_rows(name):
     w = WORKLOADS[name]
     _say(f"workload {name}")

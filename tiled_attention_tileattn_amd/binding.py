@@ -17,7 +17,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtileattn.so")
 
-EXPORTED = ("tileattn_fwd", "tileattn_fwd_f32", "tileattn_strerror", "tileattn_launch_shape")
+EXPORTED = ("tileattn_fwd", "tileattn_fwd_f16", "tileattn_fwd_f32", "tileattn_strerror",
+            "tileattn_launch_shape")
 
 STATUS = {
     0: "TILEATTN_OK",
@@ -54,6 +55,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.tileattn_fwd.argtypes = sig
     lib.tileattn_fwd.restype = i
+    lib.tileattn_fwd_f16.argtypes = sig
+    lib.tileattn_fwd_f16.restype = i
     lib.tileattn_fwd_f32.argtypes = sig
     lib.tileattn_fwd_f32.restype = i
     lib.tileattn_strerror.argtypes = [i]
@@ -69,6 +72,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 def tileattn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream) -> int:
     return load_library().tileattn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D,
                                        float(scale), int(bool(causal)), stream)
+
+
+def tileattn_fwd_f16(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream) -> int:
+    return load_library().tileattn_fwd_f16(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D,
+                                           scale, causal, stream)
 
 
 def tileattn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream) -> int:
@@ -93,13 +101,15 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
             stream=None):
     """Attention forward on the GPU: returns (o, lse).
 
-    q [B, Hq, Sq, D], k/v [B, Hkv, Sk, D]: contiguous bf16 (or fp32) tensors on
+    q [B, Hq, Sq, D], k/v [B, Hkv, Sk, D]: contiguous bf16, fp16 or fp32 tensors on
     one HIP device.  ``scale`` defaults to 1/sqrt(D).  ``out``/``lse`` may be
     preallocated ([B, Hq, Sq, D] in q's dtype, [B, Hq, Sq] fp32).  ``stream``
     is a torch stream (default: the current stream of q's device).
     """
     import torch
 
+    entry = {torch.bfloat16: tileattn_fwd, torch.float16: tileattn_fwd_f16,
+             torch.float32: tileattn_fwd_f32}
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.dim() != 4:
             raise ValueError(f"{name} must be a 4-D torch tensor")
@@ -107,8 +117,8 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
             raise ValueError(f"{name} must be on a HIP device, got {t.device}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError("q, k, v must share one dtype, bfloat16 or float32")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in entry:
+        raise ValueError("q, k, v must share one dtype: bfloat16, float16 or float32")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on the same device")
     B, Hq, Sq, D = q.shape
@@ -126,7 +136,7 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     if tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous() \
             or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 tensor [B, Hq, Sq] on q's device")
-    fn = tileattn_fwd if q.dtype == torch.bfloat16 else tileattn_fwd_f32
+    fn = entry[q.dtype]
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
         rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),

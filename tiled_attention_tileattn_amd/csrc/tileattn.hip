@@ -57,6 +57,7 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Native vector type for 16-byte staging registers: arrays of HIP's uint4
@@ -84,6 +85,26 @@ __device__ __forceinline__ float wave_pair_max(float x) {
 __device__ __forceinline__ float wave_pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The 16-bit kernel holds bf16 and fp16 operands in one bit container
+// (bf16x8); IS_F16 selects which MFMA reads the bits and how fp32 values are
+// rounded into them (round to nearest even either way).
+template <bool IS_F16>
+__device__ __forceinline__ f32x16 mfma16(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (IS_F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <bool IS_F16>
+__device__ __forceinline__ __bf16 round16(float x) {
+  if constexpr (IS_F16)
+    return __builtin_bit_cast(__bf16, (_Float16)x);
+  else
+    return (__bf16)x;
 }
 
 // Map a hardware workgroup id to (batch, query head, query tile).  Ids are
@@ -155,7 +176,7 @@ struct Bf16Tile {
 // fp32 p; p is then packed to bf16 (round to nearest even) in the B-operand
 // layout of the P*V product.  Masked scores are -inf; with c > 0 they give
 // p = exp2(-inf) = 0.
-template <int NACC>
+template <bool IS_F16, int NACC>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& m_run, float& l_run,
                                              float c, f32x16 (&acc)[NACC],
                                              bf16x8 (&pf)[2][2]) {
@@ -186,8 +207,8 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& m_run, float
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * t + e + 1], c, -mc));
         psum0 += p0;
         psum1 += p1;
-        pf[kb][t][e] = (__bf16)p0;
-        pf[kb][t][e + 1] = (__bf16)p1;
+        pf[kb][t][e] = round16<IS_F16>(p0);
+        pf[kb][t][e + 1] = round16<IS_F16>(p1);
       }
   l_run += psum0 + psum1;
 }
@@ -199,8 +220,8 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& m_run, float
 // M(j) then V(j) in the two halves of iteration j; group 1 runs V(j-1) then
 // M(j).  A barrier separates the halves, so on every SIMD one wave drives the
 // matrix core while the other works through its exponentials.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
+template <int D, bool CAUSAL, bool IS_F16>
+__global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* K,
     const uint16_t* V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Hq, int Hkv, int Sq, int Sk, float scale, int nqt, int nwg) {
@@ -324,11 +345,10 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
       if (WITH_S)
-        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kring[i % kP], qf[i >> 1],
-                                                          i < 2 ? f32x16{} : s[i & 1], 0, 0, 0);
+        s[i & 1] = mfma16<IS_F16>(kring[i % kP], qf[i >> 1], i < 2 ? f32x16{} : s[i & 1]);
       if (WITH_PV) {
         const int g = i / (D / 32), db = i % (D / 32);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vring[i % kP], pf[g >> 1][g & 1], acc[db], 0, 0, 0);
+        acc[db] = mfma16<IS_F16>(vring[i % kP], pf[g >> 1][g & 1], acc[db]);
       }
       if (i + kP < kN) {
         if (WITH_S) kring[i % kP] = k_operand(kb, i + kP);
@@ -355,7 +375,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
     }
     // c > 0 here, so a masked (-inf) score gives p = exp2(-inf) = 0 without
     // a separate masked code path.
-    softmax_tile(s, m_run, l_run, c, acc, pf);
+    softmax_tile<IS_F16>(s, m_run, l_run, c, acc, pf);
   };
 
   using TT = std::true_type;
@@ -423,7 +443,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_bf16_kernel(
       for (int g = 0; g < 4; ++g) {
         __bf16 o4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[db][4 * g + e] * inv);
+        for (int e = 0; e < 4; ++e) o4[e] = round16<IS_F16>(acc[db][4 * g + e] * inv);
         uint2 u;
         u.x = (uint32_t)__builtin_bit_cast(uint16_t, o4[0]) |
               ((uint32_t)__builtin_bit_cast(uint16_t, o4[1]) << 16);
@@ -615,11 +635,10 @@ int launch(Kern kernel, const TIn* q, const TIn* k, const TIn* v, TOut* o, float
   return e == hipSuccess ? TILEATTN_OK : TILEATTN_ERR_LAUNCH;
 }
 
-}  // namespace
-
-extern "C" int tileattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                            int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
-                            int causal, void* stream) {
+// bf16 and fp16 inputs share one kernel template (IS_F16).
+template <bool IS_F16>
+int fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+          int Hkv, int Sq, int Sk, int D, float scale, int causal, void* stream) {
   bool empty;
   const int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty);
   if (st != TILEATTN_OK || empty) return st;
@@ -629,10 +648,24 @@ extern "C" int tileattn_fwd(const void* q, const void* k, const void* v, void* o
   using T128 = Bf16Tile<128>;
   using T64 = Bf16Tile<64>;
   if (D == 128)
-    return causal ? launch<T128::kBlockM, T128::kThreads>(attn_fwd_bf16_kernel<128, true>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream)
-                  : launch<T128::kBlockM, T128::kThreads>(attn_fwd_bf16_kernel<128, false>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream);
-  return causal ? launch<T64::kBlockM, T64::kThreads>(attn_fwd_bf16_kernel<64, true>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream)
-                : launch<T64::kBlockM, T64::kThreads>(attn_fwd_bf16_kernel<64, false>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream);
+    return causal ? launch<T128::kBlockM, T128::kThreads>(attn_fwd_16_kernel<128, true, IS_F16>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream)
+                  : launch<T128::kBlockM, T128::kThreads>(attn_fwd_16_kernel<128, false, IS_F16>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream);
+  return causal ? launch<T64::kBlockM, T64::kThreads>(attn_fwd_16_kernel<64, true, IS_F16>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream)
+                : launch<T64::kBlockM, T64::kThreads>(attn_fwd_16_kernel<64, false, IS_F16>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream);
+}
+
+}  // namespace
+
+extern "C" int tileattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                            int causal, void* stream) {
+  return fwd16<false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream);
+}
+
+extern "C" int tileattn_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                                int causal, void* stream) {
+  return fwd16<true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream);
 }
 
 extern "C" int tileattn_fwd_f32(const float* q, const float* k, const float* v, float* o,

@@ -9,7 +9,7 @@ Recipe (the same for every workload):
     q = randn([B, Hq,  Sq, D]) * q_std      (float32, drawn first)
     k = randn([B, Hkv, Sk, D]) * k_std      (drawn second)
     v = randn([B, Hkv, Sk, D]) * v_std      (drawn third)
-    then cast to the workload dtype (bfloat16 casts round to nearest even).
+    then cast to the workload dtype (bfloat16 and float16 casts round to nearest even).
 A row sample for the long-context workload continues the same generator
 after v: randperm(B * Hq * Sq)[:n], flat indices into [B, Hq, Sq].
 """
@@ -33,7 +33,7 @@ class Workload:
     Sk: int
     D: int
     causal: bool
-    dtype: str          # "bf16" or "fp32"
+    dtype: str          # "bf16", "fp16" or "fp32"
     seed: int
     q_std: float = 1.0
     k_std: float = 1.0
@@ -47,7 +47,7 @@ class Workload:
 
     @property
     def torch_dtype(self):
-        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        return {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[self.dtype]
 
     def flop(self) -> float:
         """Counted attention FLOP: 4*B*Hq*Sq*Sk*D, halved when causal."""
@@ -59,7 +59,8 @@ class Workload:
 
 
 # The five workloads: a tiny fp32 case, plain multi-head bf16, causal multi-head,
-# causal grouped-query at 8K (the headline), and long-context grouped-query at 32K.
+# causal grouped-query at 8K (the headline), and long-context grouped-query at 32K;
+# plus the headline shape in fp16, the dtype of the first page's own kernel.
 WORKLOADS = {
     "tiny_fp32": Workload("tiny_fp32", 1, 1, 1, 128, 128, 64, False, "fp32", 0),
     "mha_bf16": Workload("mha_bf16", 4, 8, 8, 1024, 1024, 64, False, "bf16", 1),
@@ -67,6 +68,7 @@ WORKLOADS = {
     "causal_gqa_bf16": Workload("causal_gqa_bf16", 1, 32, 8, 8192, 8192, 128, True, "bf16", 3),
     "longctx_gqa_bf16": Workload("longctx_gqa_bf16", 1, 64, 8, 32768, 32768, 128, True, "bf16", 4,
                                  q_std=0.5, k_std=0.5, sample_rows=256),
+    "causal_gqa_fp16": Workload("causal_gqa_fp16", 1, 32, 8, 8192, 8192, 128, True, "fp16", 5),
 }
 
 HEADLINE = "causal_gqa_bf16"
