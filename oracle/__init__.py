@@ -28,6 +28,9 @@ What it computes, and where that is defined:
 Modules:
 
 * ``full_softmax`` — vectorised numpy fp64 definition (full and row-sampled).
+* ``biased``    — the same definition with an ALiBi bias and a block-sparse
+  mask (features the first page's FAQ names for the official library);
+  the readings are in its docstring.
 * ``brute``     — pure-Python triple loop with ``math.fsum``; tiny inputs only.
 
 Every function here is pinned by ``-m "not gpu"`` tests against facts that
@@ -36,6 +39,7 @@ routine, brute force); see ``tests/test_oracle_pins.py``.
 """
 
 from .full_softmax import attention, attention_rows, visible_count
+from .biased import attention_ext
 from .brute import attention_bruteforce
 
-__all__ = ["attention", "attention_rows", "visible_count", "attention_bruteforce"]
+__all__ = ["attention", "attention_rows", "visible_count", "attention_ext", "attention_bruteforce"]
