@@ -60,6 +60,59 @@ def time_workload(ta, w, steps, warmup):
     return wall_ms, float(ev.mean()), float(np.median(ev)), float(ev.min())
 
 
+def visible_pairs(mask, Hq, Sq, Sk, causal, block=64):
+    """Query-key pairs a block mask [Hm, nq, nk] (and causal) leaves visible, summed over
+    the Hq query heads (a single plane is shared by all of them): the counted
+    work of a masked workload is 4*D per pair and batch entry."""
+    m = mask.to(torch.int64)
+    if m.shape[0] == 1:
+        m = m * Hq
+    total = 0
+    for qb in range(m.shape[1]):
+        rows = min(block, Sq - qb * block)
+        for kb in range(m.shape[2]):
+            cols = min(block, Sk - kb * block)
+            if causal:
+                # pairs (i, j) of the block with j <= i
+                i0, j0 = qb * block, kb * block
+                if j0 + cols - 1 <= i0:
+                    n = rows * cols
+                elif j0 > i0 + rows - 1:
+                    n = 0
+                else:
+                    n = sum(max(0, min(cols, i - j0 + 1)) for i in range(i0, i0 + rows))
+            else:
+                n = rows * cols
+            total += int(m[:, qb, kb].sum()) * n
+    return total
+
+
+def time_ext(ta, w, steps, warmup, mask):
+    """Time the ALiBi + block-mask entry point on workload w's shape."""
+    from tiled_attention_tileattn_amd.inputs import alibi_slopes, make_inputs
+
+    q, k, v = make_inputs(w, device="cuda")
+    slopes = alibi_slopes(w.Hq).cuda()
+    pairs = visible_pairs(mask, w.Hq, w.Sq, w.Sk, w.causal)
+    mask = mask.cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    run = lambda: ta.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream,
+                             alibi_slopes=slopes, block_mask=mask)
+    for _ in range(warmup):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.median([a.elapsed_time(b) for a, b in ev]) * 1e-3
+    return t, 4.0 * w.B * w.D * pairs
+
+
 def cpu_baseline(w):
     """Time the fp64 oracle on the whole workload on this host's cores.
 
@@ -149,6 +202,19 @@ def main():
             wall, mean, med, mn = time_workload(ta, w, st, wu)
             log(f"{name}: median {med*1e3:.1f} us min {mn*1e3:.1f} us "
                 f"-> {w.flop()/med/1e9:.1f} TFLOP/s ({w.flop()/med/1e9/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
+
+        # ALiBi bias + block masks on the headline shape; work counted over
+        # the visible query-key pairs only.
+        from tiled_attention_tileattn_amd.inputs import random_block_mask, window_block_mask
+
+        w = WORKLOADS[HEADLINE]
+        masks = {"random 50% per-head block mask": random_block_mask(w.Hq, w.Sq, w.Sk, seed=w.seed + 100,
+                                                                     p_visible=0.5),
+                 "1024-key local window + sink block": window_block_mask(w.Sq, w.Sk, 16)}
+        for what, mask in masks.items():
+            t, flop = time_ext(ta, w, args.steps, args.warmup, mask)
+            log(f"{HEADLINE} + ALiBi + {what}: median {t*1e6:.1f} us -> {flop/t/1e12:.1f} TFLOP/s "
+                f"on visible pairs ({flop/t/1e12/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
 
     w = WORKLOADS[HEADLINE]
     wall, mean, med, mn = time_workload(ta, w, args.steps, args.warmup)

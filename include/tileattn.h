@@ -92,6 +92,38 @@ int tileattn_fwd_f16(const void* q, const void* k, const void* v, void* o, float
                      float scale, int causal, void* stream);
 
 /*
+ * 16-bit attention forward with an ALiBi bias and/or a block-sparse mask.
+ * The first page's FAQ names both (with causal masking) as what the official
+ * flash-attention library adds over its tutorial kernel; it does not define
+ * them, so this entry point takes the plainest readings:
+ *   - ALiBi ("Train Short, Test Long: Attention with Linear Biases"): a slope
+ *     m_h per query head adds a bias linear in the query-key distance to the
+ *     scaled score:  s_ij = scale * <q_i, k_j> + b_ij  with
+ *     b_ij = -m_h * (i - j) when causal, -m_h * |i - j| otherwise.
+ *   - block mask: uint8 map [mask_heads, ceil(Sq/64), ceil(Sk/64)]; block
+ *     (qb, kb) is visible iff its byte is nonzero (query rows 64*qb..64*qb+63,
+ *     keys 64*kb..64*kb+63).  mask_heads is 1 (one map for every head and
+ *     batch) or Hq (query head h uses plane h).  It combines with causal (a
+ *     key must pass both).  Tiles no query block of a workgroup can see are
+ *     neither loaded nor computed.
+ *   - a row with no visible key gets o = 0 and lse = -inf.
+ *   q, k, v, o as for tileattn_fwd (is_f16 = 0: bf16, else fp16); lse is the
+ *   natural log of the softmax denominator of the biased scaled scores.
+ *   alibi_slopes : NULL (no bias) or device pointer to Hq fp32 slopes
+ *                  (4-byte aligned).
+ *   block_mask   : NULL (no mask) or device pointer to the uint8 map above.
+ * Extra errors: TILEATTN_ERR_BAD_SHAPE if block_mask is given and mask_heads
+ * is not 1 or Hq; TILEATTN_ERR_TOO_LARGE if block_mask is given and
+ * Sk > 131072 (the per-workgroup tile list holds 2048 tiles);
+ * TILEATTN_ERR_ALIGNMENT for a misaligned alibi_slopes.
+ */
+int tileattn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                     float scale, int causal, const float* alibi_slopes,
+                     const unsigned char* block_mask, int mask_heads, int is_f16,
+                     void* stream);
+
+/*
  * float32 attention forward: the same contract as tileattn_fwd with fp32
  * q, k, v and o.  Both products use fp32 matrix-core instructions and the
  * probabilities stay fp32 (there is no narrower value dtype to cast them to).

@@ -1,0 +1,47 @@
+"""Host-side logic of bench.py (CPU only): the work count of masked workloads
+and the block-mask recipes it times."""
+
+import sys
+from pathlib import Path
+
+import numpy as np
+import torch
+
+sys.path.insert(0, str(Path(__file__).resolve().parents[1]))
+import bench  # noqa: E402
+from tiled_attention_tileattn_amd.inputs import random_block_mask, window_block_mask  # noqa: E402
+
+
+def _brute_pairs(mask, Hq, Sq, Sk, causal, block=64):
+    m = mask.numpy().astype(bool)
+    i = np.arange(Sq)[:, None]
+    j = np.arange(Sk)[None, :]
+    total = 0
+    for h in range(Hq):
+        plane = m[h if m.shape[0] == Hq else 0]
+        vis = plane[i // block, j // block]
+        if causal:
+            vis = vis & (j <= i)
+        total += int(vis.sum())
+    return total
+
+
+def test_visible_pairs_matches_brute_force():
+    for Hq, Sq, Sk, causal, per_head in [(3, 200, 200, True, True), (2, 130, 257, False, False),
+                                         (4, 300, 100, True, False), (1, 65, 65, True, True)]:
+        mask = random_block_mask(Hq if per_head else 1, Sq, Sk, seed=Sq + Sk, p_visible=0.5)
+        assert bench.visible_pairs(mask, Hq, Sq, Sk, causal) == _brute_pairs(mask, Hq, Sq, Sk, causal)
+
+
+def test_visible_pairs_of_full_mask_is_dense_count():
+    ones = torch.ones(1, 4, 4, dtype=torch.uint8)
+    assert bench.visible_pairs(ones, 5, 256, 256, True) == 5 * 256 * 257 // 2
+    assert bench.visible_pairs(ones, 5, 256, 256, False) == 5 * 256 * 256
+
+
+def test_window_mask_shape():
+    m = window_block_mask(1000, 1000, 3)[0].numpy()
+    assert m.shape == (16, 16)
+    for qb in range(16):
+        seen = set(np.nonzero(m[qb])[0])
+        assert seen == {0} | set(range(max(0, qb - 2), qb + 1))

@@ -1,7 +1,8 @@
 """tileattn: exact attention forward for MI355X (gfx950), HIP kernels behind a C ABI.
 
 ``forward(q, k, v, causal, scale) -> (o, lse)`` is the torch-facing entry;
-``tileattn_fwd`` / ``tileattn_fwd_f16`` / ``tileattn_fwd_f32`` / ``tileattn_strerror`` /
+``tileattn_fwd`` / ``tileattn_fwd_f16`` / ``tileattn_fwd_ext`` / ``tileattn_fwd_f32`` /
+``tileattn_strerror`` /
 ``tileattn_launch_shape`` mirror the C functions of ``include/tileattn.h``.
 The shared library is loaded on first use and must have been built
 (``python -m tiled_attention_tileattn_amd.build``); there is no fallback.
@@ -14,6 +15,7 @@ from .binding import (  # noqa: F401
     forward,
     load_library,
     tileattn_fwd,
+    tileattn_fwd_ext,
     tileattn_fwd_f16,
     tileattn_fwd_f32,
     tileattn_launch_shape,

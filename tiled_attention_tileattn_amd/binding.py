@@ -17,8 +17,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtileattn.so")
 
-EXPORTED = ("tileattn_fwd", "tileattn_fwd_f16", "tileattn_fwd_f32", "tileattn_strerror",
-            "tileattn_launch_shape")
+EXPORTED = ("tileattn_fwd", "tileattn_fwd_f16", "tileattn_fwd_ext", "tileattn_fwd_f32",
+            "tileattn_strerror", "tileattn_launch_shape")
 
 STATUS = {
     0: "TILEATTN_OK",
@@ -57,6 +57,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tileattn_fwd.restype = i
     lib.tileattn_fwd_f16.argtypes = sig
     lib.tileattn_fwd_f16.restype = i
+    lib.tileattn_fwd_ext.argtypes = sig[:13] + [vp, vp, i, i, vp]
+    lib.tileattn_fwd_ext.restype = i
     lib.tileattn_fwd_f32.argtypes = sig
     lib.tileattn_fwd_f32.restype = i
     lib.tileattn_strerror.argtypes = [i]
@@ -79,6 +81,12 @@ def tileattn_fwd_f16(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stre
                                            scale, causal, stream)
 
 
+def tileattn_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, alibi_slopes,
+                     block_mask, mask_heads, is_f16, stream) -> int:
+    return load_library().tileattn_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal,
+                                           alibi_slopes, block_mask, mask_heads, is_f16, stream)
+
+
 def tileattn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream) -> int:
     return load_library().tileattn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D,
                                            float(scale), int(bool(causal)), stream)
@@ -98,13 +106,17 @@ def tileattn_launch_shape(dtype_bytes, B, Hq, Hkv, Sq, Sk, D, causal):
 
 # ---- torch convenience wrapper ----------------------------------------------
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
-            stream=None):
+            stream=None, alibi_slopes=None, block_mask=None):
     """Attention forward on the GPU: returns (o, lse).
 
     q [B, Hq, Sq, D], k/v [B, Hkv, Sk, D]: contiguous bf16, fp16 or fp32 tensors on
     one HIP device.  ``scale`` defaults to 1/sqrt(D).  ``out``/``lse`` may be
     preallocated ([B, Hq, Sq, D] in q's dtype, [B, Hq, Sq] fp32).  ``stream``
     is a torch stream (default: the current stream of q's device).
+
+    ``alibi_slopes`` (float32 [Hq]) and/or ``block_mask`` (uint8
+    [1 or Hq, ceil(Sq/64), ceil(Sk/64)]), both on q's device, select
+    ``tileattn_fwd_ext`` (bf16 or fp16 inputs only).
     """
     import torch
 
@@ -136,11 +148,36 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     if tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous() \
             or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 tensor [B, Hq, Sq] on q's device")
-    fn = entry[q.dtype]
+    ext = alibi_slopes is not None or block_mask is not None
+    if ext:
+        if q.dtype not in (torch.bfloat16, torch.float16):
+            raise ValueError("alibi_slopes / block_mask need bfloat16 or float16 inputs")
+        if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32
+                                         or tuple(alibi_slopes.shape) != (Hq,)
+                                         or not alibi_slopes.is_contiguous()
+                                         or alibi_slopes.device != q.device):
+            raise ValueError("alibi_slopes must be a contiguous float32 tensor [Hq] on q's device")
+        mask_heads = 1
+        if block_mask is not None:
+            nq, nk = -(-Sq // 64), -(-Sk // 64)
+            if (block_mask.dtype != torch.uint8 or block_mask.dim() != 3
+                    or block_mask.shape[0] not in (1, Hq) or tuple(block_mask.shape[1:]) != (nq, nk)
+                    or not block_mask.is_contiguous() or block_mask.device != q.device):
+                raise ValueError(f"block_mask must be a contiguous uint8 tensor [1 or Hq, {nq}, {nk}] "
+                                 "on q's device")
+            mask_heads = block_mask.shape[0]
+    fn = tileattn_fwd_ext if ext else entry[q.dtype]
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
-        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                B, Hq, Hkv, Sq, Sk, D, scale, causal, s.cuda_stream)
+        if ext:
+            rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, Hq, Hkv, Sq, Sk, D, scale, causal,
+                    None if alibi_slopes is None else alibi_slopes.data_ptr(),
+                    None if block_mask is None else block_mask.data_ptr(), mask_heads,
+                    int(q.dtype == torch.float16), s.cuda_stream)
+        else:
+            rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, Hq, Hkv, Sq, Sk, D, scale, causal, s.cuda_stream)
     if rc != 0:
         raise TileAttnError(rc, fn.__name__)
     return out, lse

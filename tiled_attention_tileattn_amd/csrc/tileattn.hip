@@ -75,6 +75,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format,
 // no swizzle, no stride): loads past num_records return 0.
 constexpr int kBufferFlags = 0x00020000;
+// Capacity of the per-workgroup tile list of block-masked calls: Sk <= 64 * this.
+constexpr int kMaxMaskedTiles = 2048;
 
 __device__ __forceinline__ float wave_pair_max(float x) {
   // Lanes l and l^32 hold the same query row; combine their partial maxima.
@@ -176,7 +178,7 @@ struct Bf16Tile {
 // fp32 p; p is then packed to bf16 (round to nearest even) in the B-operand
 // layout of the P*V product.  Masked scores are -inf; with c > 0 they give
 // p = exp2(-inf) = 0.
-template <bool IS_F16, int NACC>
+template <bool IS_F16, bool GUARD, int NACC>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& m_run, float& l_run,
                                              float c, f32x16 (&acc)[NACC],
                                              bf16x8 (&pf)[2][2]) {
@@ -195,7 +197,9 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& m_run, float
 #pragma unroll
     for (int i = 0; i < NACC; ++i) acc[i] *= alpha;
   }
-  const float mc = m_run * c;
+  // GUARD: a row that has seen no visible key yet keeps m_run = -inf; its
+  // masked scores must still give p = 0, not exp2(-inf + inf).
+  const float mc = (GUARD && m_run == -INFINITY) ? 0.f : m_run * c;
   float psum0 = 0.f, psum1 = 0.f;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -220,11 +224,12 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& m_run, float
 // M(j) then V(j) in the two halves of iteration j; group 1 runs V(j-1) then
 // M(j).  A barrier separates the halves, so on every SIMD one wave drives the
 // matrix core while the other works through its exponentials.
-template <int D, bool CAUSAL, bool IS_F16>
+template <int D, bool CAUSAL, bool IS_F16, bool EXT>
 __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* K,
     const uint16_t* V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int Hq, int Hkv, int Sq, int Sk, float scale, int nqt, int nwg) {
+    int Hq, int Hkv, int Sq, int Sk, float scale, int nqt, int nwg,
+    const float* __restrict__ slopes, const unsigned char* __restrict__ bmask, int mask_heads) {
   using T = Bf16Tile<D>;
   static_assert(T::kWaves == 8, "two groups of four waves");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::kKBytes + 2 * T::kVBytes];
@@ -254,6 +259,44 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     const int last_row = min(q0 + T::kBlockM - 1, Sq - 1);
     nkt = min(nkt, last_row / kBlockN + 1);
   }
+
+  // Key tiles the workgroup visits.  Without a block mask: tiles 0..nkt-1.
+  // With one (EXT): the tiles that any of the workgroup's four 64-row query
+  // blocks may see, in order, compacted into an LDS list by wave 0; entry =
+  // tile index (bits 0-11) | visibility of query block i (bit 12 + i).
+  __shared__ unsigned short tlist[EXT ? kMaxMaskedTiles : 1];
+  __shared__ int tcount;
+  const bool has_mask = EXT && bmask != nullptr;
+  int nt = nkt;
+  if (has_mask) {
+    if (wave == 0) {
+      const int nqb = (Sq + kBlockN - 1) / kBlockN, nkb = (Sk + kBlockN - 1) / kBlockN;
+      const unsigned char* plane = bmask + (size_t)(mask_heads == Hq ? hq : 0) * nqb * nkb;
+      const int qb0 = q0 / kBlockN;
+      int count = 0;
+      for (int base = 0; base < nkt; base += 64) {
+        const int kb = base + lane;
+        unsigned bits = 0;
+        if (kb < nkt) {
+#pragma unroll
+          for (int i = 0; i < T::kBlockM / kBlockN; ++i)
+            if (qb0 + i < nqb && plane[(size_t)(qb0 + i) * nkb + kb] != 0) bits |= 1u << i;
+        }
+        const unsigned long long vis = __ballot(bits != 0);
+        const int pos = count + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(vis >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((unsigned)vis, 0u));
+        if (bits != 0) tlist[pos] = (unsigned short)(kb | (bits << 12));
+        count += __popcll(vis);
+      }
+      if (lane == 0) tcount = count;
+    }
+    __syncthreads();
+    nt = tcount;
+  }
+  auto tile = [&](int j) -> int { return has_mask ? (int)(tlist[j] & 0xFFF) : j; };
+  // This wave's 64-row query block may see tile j (block mask).
+  auto wave_sees = [&](int j) -> bool { return !has_mask || ((tlist[j] >> (12 + (wave >> 1))) & 1); };
+  const float slope = (EXT && slopes != nullptr) ? slopes[hq] : 0.f;
 
   bf16x8 qf[D / 16];
   {
@@ -323,7 +366,10 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
   // exp2 argument scale, scale*log2(e), kept >= the smallest normal float: a
   // zero (or tiny) scale then still gives every visible key p = exp2(~0) = 1
   // exactly, as scale = 0 does, while masked -inf scores keep p = 0.
-  const float c = fmaxf(scale * kLog2e, 1.17549435e-38f);
+  //
+  // EXT works in scaled units instead: the kernel adds the bias to
+  // scale * s and exponentiates with c = log2(e).
+  const float c = EXT ? kLog2e : fmaxf(scale * kLog2e, 1.17549435e-38f);
 
   constexpr int kN = 2 * (D / 16);  // MFMAs of each product per tile
   static_assert(kN == 4 * (D / 32), "both products take the same number of MFMAs");
@@ -331,7 +377,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
 
   // Matrix phase: S_j (WITH_S) and acc += V_{j-1}^T P_{j-1}^T (WITH_PV),
   // MFMA by MFMA alternating, operands read kP steps ahead.
-  auto matrix_phase = [&](auto with_s_c, auto with_pv_c, int j) {
+  auto matrix_body = [&](auto with_s_c, auto with_pv_c, int j) {
     constexpr bool WITH_S = decltype(with_s_c)::value;
     constexpr bool WITH_PV = decltype(with_pv_c)::value;
     const int kb = kslot(j) + k_lane_off, vb = vslot(j - 1) + v_lane_off;
@@ -358,15 +404,48 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     }
     if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
   };
+  // With a block mask, a wave skips the products of the tiles its query
+  // block cannot see: their probabilities would all be 0.
+  auto matrix_phase = [&](auto with_s_c, auto with_pv_c, int j) {
+    using TT_ = std::true_type;
+    using FF_ = std::false_type;
+    constexpr bool WITH_S = decltype(with_s_c)::value;
+    constexpr bool WITH_PV = decltype(with_pv_c)::value;
+    if constexpr (!EXT) {
+      matrix_body(with_s_c, with_pv_c, j);
+    } else {
+      // Two independent products, one after the other, each behind its own
+      // wave-uniform branch (one body with both would need four variants).
+      if (WITH_S && wave_sees(j)) matrix_body(TT_{}, FF_{}, j);
+      if (WITH_PV && wave_sees(j - 1)) matrix_body(FF_{}, TT_{}, j);
+    }
+  };
 
   // Vector phase: mask tile j where needed, online softmax, pack P_j.
   // Tiles past a causal wave's diagonal come out fully masked (p = 0): the
   // tile max is -inf, the reference max stays, and acc and l are unchanged.
   auto vector_phase = [&](int j) {
-    const int key0 = j * kBlockN;
-    const bool need_mask = (CAUSAL && key0 + kBlockN - 1 > qw) || (key0 + kBlockN > Sk);
+    // Block mask: a tile this wave cannot see changes nothing (its matrix
+    // phases skip it too).
+    if (EXT && !wave_sees(j)) return;
+    const int key0 = tile(j) * kBlockN;
+    if constexpr (EXT) {
+      // Scaled score plus the linear bias: key - row = d, bias = slope * d
+      // (causal: every visible d <= 0) or -slope * |d| (non-causal).
+      const float d0 = (float)(key0 + 4 * half - my_row);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float d = d0 + (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
+          const float bias = CAUSAL ? slope * d : -slope * fabsf(d);
+          s[kb][r] = fmaf(s[kb][r], scale, bias);
+        }
+    }
+    const bool sees = wave_sees(j);
+    const bool need_mask = (CAUSAL && key0 + kBlockN - 1 > qw) || (key0 + kBlockN > Sk) || !sees;
     if (need_mask) {
-      const int lim = (CAUSAL ? min(Sk - 1, my_row) : Sk - 1) - key0 - 4 * half;
+      const int lim = !sees ? -kBlockN : (CAUSAL ? min(Sk - 1, my_row) : Sk - 1) - key0 - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -375,7 +454,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     }
     // c > 0 here, so a masked (-inf) score gives p = exp2(-inf) = 0 without
     // a separate masked code path.
-    softmax_tile<IS_F16>(s, m_run, l_run, c, acc, pf);
+    softmax_tile<IS_F16, EXT>(s, m_run, l_run, c, acc, pf);
   };
 
   using TT = std::true_type;
@@ -391,9 +470,9 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
   // Both write the slots that K_{j-1} and V_{j-2} left; the closing barrier
   // publishes the whole tile for iteration j+1.
   auto iteration0 = [&](int j, auto first, auto second) {
-    const bool ld_k = j + 1 < nkt, ld_v = j < nkt;
-    if (ld_k) load_rows(krsrc, j + 1, kreg);
-    if (ld_v) load_rows(vrsrc, j, vreg);
+    const bool ld_k = j + 1 < nt, ld_v = j < nt;
+    if (ld_k) load_rows(krsrc, tile(j + 1), kreg);
+    if (ld_v) load_rows(vrsrc, tile(j), vreg);
     first();
     __builtin_amdgcn_s_barrier();
     second();
@@ -402,39 +481,44 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     __syncthreads();
   };
   auto iteration1 = [&](int j, auto first, auto second) {
-    if (j + 1 < nkt) store_rows(kslot(j + 1), T::kKPitch, kreg);
-    if (j < nkt) store_rows(vslot(j), T::kVPitch, vreg);
-    if (j + 2 < nkt) load_rows(krsrc, j + 2, kreg);
-    if (j + 1 < nkt) load_rows(vrsrc, j + 1, vreg);
+    if (j + 1 < nt) store_rows(kslot(j + 1), T::kKPitch, kreg);
+    if (j < nt) store_rows(vslot(j), T::kVPitch, vreg);
+    if (j + 2 < nt) load_rows(krsrc, tile(j + 2), kreg);
+    if (j + 1 < nt) load_rows(vrsrc, tile(j + 1), vreg);
     first();
     __builtin_amdgcn_s_barrier();
     second();
     __syncthreads();
   };
 
-  load_rows(krsrc, 0, kreg);
-  store_rows(kslot(0), T::kKPitch, kreg);
-  if (group == 1) {
-    if (nkt > 1) load_rows(krsrc, 1, kreg);
-    load_rows(vrsrc, 0, vreg);
-  }
-  __syncthreads();
+  // A workgroup whose block mask shows it no tile skips the loop: its rows
+  // have no visible key (o = 0, lse = -inf below).
+  if (!EXT || nt > 0) {
+    load_rows(krsrc, tile(0), kreg);
+    store_rows(kslot(0), T::kKPitch, kreg);
+    if (group == 1) {
+      if (nt > 1) load_rows(krsrc, tile(1), kreg);
+      load_rows(vrsrc, tile(0), vreg);
+    }
+    __syncthreads();
 
-  if (group == 0) {
-    iteration0(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
-    for (int j = 1; j < nkt; ++j)
-      iteration0(j, [&] { matrix_phase(TT{}, TT{}, j); }, [&] { vector_phase(j); });
-    iteration0(nkt, [&] { matrix_phase(FF{}, TT{}, nkt); }, [&] {});
-  } else {
-    iteration1(0, [&] {}, [&] { matrix_phase(TT{}, FF{}, 0); });
-    for (int j = 1; j < nkt; ++j)
-      iteration1(j, [&] { vector_phase(j - 1); }, [&] { matrix_phase(TT{}, TT{}, j); });
-    iteration1(nkt, [&] { vector_phase(nkt - 1); }, [&] { matrix_phase(FF{}, TT{}, nkt); });
+    if (group == 0) {
+      iteration0(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
+      for (int j = 1; j < nt; ++j)
+        iteration0(j, [&] { matrix_phase(TT{}, TT{}, j); }, [&] { vector_phase(j); });
+      iteration0(nt, [&] { matrix_phase(FF{}, TT{}, nt); }, [&] {});
+    } else {
+      iteration1(0, [&] {}, [&] { matrix_phase(TT{}, FF{}, 0); });
+      for (int j = 1; j < nt; ++j)
+        iteration1(j, [&] { vector_phase(j - 1); }, [&] { matrix_phase(TT{}, TT{}, j); });
+      iteration1(nt, [&] { vector_phase(nt - 1); }, [&] { matrix_phase(FF{}, TT{}, nt); });
+    }
   }
 
   // ---- epilogue: O = acc / l, lse = m*scale + ln l --------------------------
   const float l_tot = wave_pair_sum(l_run);
-  const float inv = 1.0f / l_tot;
+  // EXT: a row with no visible key (l = 0, m = -inf) gets o = 0, lse = -inf.
+  const float inv = (EXT && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
   if (my_row < Sq) {
     uint16_t* orow = O + (q_head + my_row) * D;
 #pragma unroll
@@ -451,7 +535,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
               ((uint32_t)__builtin_bit_cast(uint16_t, o4[3]) << 16);
         *reinterpret_cast<uint2*>(orow + db * 32 + 8 * g + 4 * half) = u;
       }
-    if (half == 0) LSE[q_head + my_row] = m_run * scale + logf(l_tot);
+    if (half == 0) LSE[q_head + my_row] = m_run * (EXT ? 1.f : scale) + logf(l_tot);
   }
 }
 
@@ -635,23 +719,46 @@ int launch(Kern kernel, const TIn* q, const TIn* k, const TIn* v, TOut* o, float
   return e == hipSuccess ? TILEATTN_OK : TILEATTN_ERR_LAUNCH;
 }
 
-// bf16 and fp16 inputs share one kernel template (IS_F16).
-template <bool IS_F16>
+// The 16-bit kernel takes three more arguments (bias slopes, block mask and
+// its head count); the plain entry points pass none.
+template <int BLOCK_M, int THREADS, typename Kern>
+int launch16(Kern kernel, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+             float* lse, int B, int Hq, int Hkv, int Sq, int Sk, float scale,
+             const float* slopes, const unsigned char* bmask, int mask_heads, void* stream) {
+  const int nqt = (Sq + BLOCK_M - 1) / BLOCK_M;
+  const int nwg = B * Hq * nqt;
+  void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&Hq,
+                  (void*)&Hkv, (void*)&Sq, (void*)&Sk, (void*)&scale, (void*)&nqt, (void*)&nwg,
+                  (void*)&slopes, (void*)&bmask, (void*)&mask_heads};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(nwg), dim3(THREADS),
+                                 args, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TILEATTN_OK : TILEATTN_ERR_LAUNCH;
+}
+
+// bf16 and fp16 inputs share one kernel template (IS_F16); EXT adds the
+// linear bias and the block mask.
+template <bool IS_F16, bool EXT>
 int fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-          int Hkv, int Sq, int Sk, int D, float scale, int causal, void* stream) {
+          int Hkv, int Sq, int Sk, int D, float scale, int causal, const float* slopes,
+          const unsigned char* bmask, int mask_heads, void* stream) {
   bool empty;
   const int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty);
-  if (st != TILEATTN_OK || empty) return st;
+  if (st != TILEATTN_OK) return st;
+  if (EXT) {
+    if (bmask != nullptr && mask_heads != 1 && mask_heads != Hq) return TILEATTN_ERR_BAD_SHAPE;
+    if (bmask != nullptr && Sk > 64 * kMaxMaskedTiles) return TILEATTN_ERR_TOO_LARGE;
+    if (slopes != nullptr && (reinterpret_cast<uintptr_t>(slopes) & 3u) != 0) return TILEATTN_ERR_ALIGNMENT;
+  }
+  if (empty) return TILEATTN_OK;
   auto qq = static_cast<const uint16_t*>(q), kk = static_cast<const uint16_t*>(k),
        vv = static_cast<const uint16_t*>(v);
   auto oo = static_cast<uint16_t*>(o);
-  using T128 = Bf16Tile<128>;
-  using T64 = Bf16Tile<64>;
-  if (D == 128)
-    return causal ? launch<T128::kBlockM, T128::kThreads>(attn_fwd_16_kernel<128, true, IS_F16>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream)
-                  : launch<T128::kBlockM, T128::kThreads>(attn_fwd_16_kernel<128, false, IS_F16>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream);
-  return causal ? launch<T64::kBlockM, T64::kThreads>(attn_fwd_16_kernel<64, true, IS_F16>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream)
-                : launch<T64::kBlockM, T64::kThreads>(attn_fwd_16_kernel<64, false, IS_F16>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, stream);
+#define TILEATTN_L16(DD, CC) launch16<Bf16Tile<DD>::kBlockM, Bf16Tile<DD>::kThreads>(               \
+      attn_fwd_16_kernel<DD, CC, IS_F16, EXT>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, \
+      slopes, bmask, mask_heads, stream)
+  if (D == 128) return causal ? TILEATTN_L16(128, true) : TILEATTN_L16(128, false);
+  return causal ? TILEATTN_L16(64, true) : TILEATTN_L16(64, false);
+#undef TILEATTN_L16
 }
 
 }  // namespace
@@ -659,13 +766,26 @@ int fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int 
 extern "C" int tileattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
                             int causal, void* stream) {
-  return fwd16<false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream);
+  return fwd16<false, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, nullptr, nullptr, 1,
+                             stream);
 }
 
 extern "C" int tileattn_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
                                 int causal, void* stream) {
-  return fwd16<true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream);
+  return fwd16<true, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, nullptr, nullptr, 1,
+                            stream);
+}
+
+extern "C" int tileattn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                                int causal, const float* alibi_slopes,
+                                const unsigned char* block_mask, int mask_heads, int is_f16,
+                                void* stream) {
+  return is_f16 ? fwd16<true, true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal,
+                                    alibi_slopes, block_mask, mask_heads, stream)
+                : fwd16<false, true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal,
+                                     alibi_slopes, block_mask, mask_heads, stream);
 }
 
 extern "C" int tileattn_fwd_f32(const float* q, const float* k, const float* v, float* o,

@@ -105,3 +105,37 @@ def random_qkv(B, Hq, Hkv, Sq, Sk, D, dtype="bf16", seed=0, q_std=1.0, k_std=1.0
     """Ad-hoc shapes for tests, same recipe as ``make_inputs``."""
     w = Workload("adhoc", B, Hq, Hkv, Sq, Sk, D, False, dtype, seed, q_std, k_std, v_std)
     return make_inputs(w, device=device)
+
+
+def alibi_slopes(Hq: int, base: float = 8.0) -> torch.Tensor:
+    """ALiBi slopes, the geometric sequence 2^(-base*h/Hq), h = 1..Hq, as float32.
+
+    This is the slope recipe of "Train Short, Test Long: Attention with
+    Linear Biases"; the kernel takes any slopes, these are the inputs used.
+    """
+    return torch.tensor([2.0 ** (-base * (h + 1) / Hq) for h in range(Hq)], dtype=torch.float32)
+
+
+def random_block_mask(mask_heads: int, Sq: int, Sk: int, seed: int, p_visible: float = 0.5,
+                      block: int = 64) -> torch.Tensor:
+    """Seeded uint8 block map [mask_heads, ceil(Sq/block), ceil(Sk/block)].
+
+    Each block is visible with probability p_visible (numpy default_rng);
+    key block 0 is always visible, so no query row is left without a key.
+    """
+    rng = np.random.default_rng(seed)
+    nq, nk = -(-Sq // block), -(-Sk // block)
+    m = (rng.random((mask_heads, nq, nk)) < p_visible).astype(np.uint8)
+    m[:, :, 0] = 1
+    return torch.from_numpy(m).contiguous()
+
+
+def window_block_mask(Sq: int, Sk: int, window_blocks: int, block: int = 64) -> torch.Tensor:
+    """Local-window block map [1, nq, nk]: query block qb sees key blocks
+    qb - window_blocks + 1 .. qb, plus key block 0 (a "sink" every row keeps)."""
+    nq, nk = -(-Sq // block), -(-Sk // block)
+    m = np.zeros((1, nq, nk), dtype=np.uint8)
+    for qb in range(nq):
+        m[0, qb, max(0, qb - window_blocks + 1): min(nk, qb + 1)] = 1
+        m[0, qb, 0] = 1
+    return torch.from_numpy(m).contiguous()
