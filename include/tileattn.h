@@ -110,7 +110,10 @@ int tileattn_fwd_f16(const void* q, const void* k, const void* v, void* o, float
  *   q, k, v, o as for tileattn_fwd (is_f16 = 0: bf16, else fp16); lse is the
  *   natural log of the softmax denominator of the biased scaled scores.
  *   alibi_slopes : NULL (no bias) or device pointer to Hq fp32 slopes
- *                  (4-byte aligned).
+ *                  (4-byte aligned), |m_h| <= 1e6 (the kernel carries the
+ *                  bias divided by scale).  With slopes, a scale below 2^-64
+ *                  (zero included) is taken as 0: the scores are the bias
+ *                  alone.
  *   block_mask   : NULL (no mask) or device pointer to the uint8 map above.
  * Extra errors: TILEATTN_ERR_BAD_SHAPE if block_mask is given and mask_heads
  * is not 1 or Hq; TILEATTN_ERR_TOO_LARGE if block_mask is given and

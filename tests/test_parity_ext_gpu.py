@@ -38,13 +38,17 @@ def _device():
 
 
 def _run(B, Hq, Hkv, Sq, Sk, D, causal, dtype, seed, use_slopes, mask_heads, p_visible=0.6,
-         empty_qblocks=()):
+         empty_qblocks=(), scale=None):
+    """use_slopes: False, True (the geometric slopes) or a list of Hq slopes."""
     what = (f"B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} D={D} causal={causal} {dtype} seed={seed} "
-            f"slopes={use_slopes} mask_heads={mask_heads}")
+            f"slopes={use_slopes} mask_heads={mask_heads} scale={scale}")
     _say(what)
     q, k, v = random_qkv(B, Hq, Hkv, Sq, Sk, D, dtype=dtype, seed=seed)
-    scale = float(np.float32(1.0 / math.sqrt(D)))
-    slopes = alibi_slopes(Hq) if use_slopes else None
+    scale = float(np.float32(1.0 / math.sqrt(D))) if scale is None else scale
+    if isinstance(use_slopes, (list, tuple)):
+        slopes = torch.tensor(use_slopes, dtype=torch.float32)
+    else:
+        slopes = alibi_slopes(Hq) if use_slopes else None
     mask = None
     if mask_heads:
         mask = random_block_mask(mask_heads, Sq, Sk, seed=seed + 1, p_visible=p_visible)
@@ -124,3 +128,18 @@ def test_ext_headline_shape_slice():
     # a 50% block mask, against the full oracle on those heads
     _run(1, 4, 1, 8192, 8192, 128, True, "bf16", seed=93, use_slopes=True, mask_heads=4,
          p_visible=0.5)
+
+
+@pytest.mark.parametrize("scale", [0.0, 1e-30, 1.0])
+@pytest.mark.parametrize("mask_heads", [0, 2])
+def test_ext_scale_edges(scale, mask_heads):
+    # scale 0 (and below 2^-64): the scores are the bias alone
+    _run(1, 2, 1, 200, 330, 64, True, "bf16", seed=94, use_slopes=True, mask_heads=mask_heads,
+         scale=scale)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ext_steep_slopes(causal):
+    # slopes up to 4 per key: the weight sits on the few keys next to the row
+    _run(1, 4, 2, 333, 333, 128, causal, "bf16", seed=95, use_slopes=[4.0, 1.0, 0.25, 0.0],
+         mask_heads=0)

@@ -224,7 +224,9 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& m_run, float
 // M(j) then V(j) in the two halves of iteration j; group 1 runs V(j-1) then
 // M(j).  A barrier separates the halves, so on every SIMD one wave drives the
 // matrix core while the other works through its exponentials.
-template <int D, bool CAUSAL, bool IS_F16, bool EXT>
+// MASK: a block mask (tile list, per-wave skipping, rows with no visible key);
+// ALIBI: the linear bias.  The plain kernel has neither.
+template <int D, bool CAUSAL, bool IS_F16, bool MASK, bool ALIBI>
 __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* K,
     const uint16_t* V, uint16_t* __restrict__ O, float* __restrict__ LSE,
@@ -261,14 +263,13 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
   }
 
   // Key tiles the workgroup visits.  Without a block mask: tiles 0..nkt-1.
-  // With one (EXT): the tiles that any of the workgroup's four 64-row query
+  // With one: the tiles that any of the workgroup's four 64-row query
   // blocks may see, in order, compacted into an LDS list by wave 0; entry =
   // tile index (bits 0-11) | visibility of query block i (bit 12 + i).
-  __shared__ unsigned short tlist[EXT ? kMaxMaskedTiles : 1];
+  __shared__ unsigned short tlist[MASK ? kMaxMaskedTiles : 1];
   __shared__ int tcount;
-  const bool has_mask = EXT && bmask != nullptr;
   int nt = nkt;
-  if (has_mask) {
+  if (MASK) {
     if (wave == 0) {
       const int nqb = (Sq + kBlockN - 1) / kBlockN, nkb = (Sk + kBlockN - 1) / kBlockN;
       const unsigned char* plane = bmask + (size_t)(mask_heads == Hq ? hq : 0) * nqb * nkb;
@@ -293,14 +294,22 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     __syncthreads();
     nt = tcount;
   }
-  auto tile = [&](int j) -> int { return has_mask ? (int)(tlist[j] & 0xFFF) : j; };
+  auto tile = [&](int j) -> int { return MASK ? (int)(tlist[j] & 0xFFF) : j; };
   // This wave's 64-row query block may see tile j (block mask).
-  auto wave_sees = [&](int j) -> bool { return !has_mask || ((tlist[j] >> (12 + (wave >> 1))) & 1); };
-  const float slope = (EXT && slopes != nullptr) ? slopes[hq] : 0.f;
+  auto wave_sees = [&](int j) -> bool { return !MASK || ((tlist[j] >> (12 + (wave >> 1))) & 1); };
+
+  // With the bias, scores are kept in units of 1/kscale: the S product
+  // starts from bias/kscale instead of 0 (see bias_init), so the softmax and
+  // lse below are those of the plain kernel with kscale for scale.  A scale
+  // under 2^-64 (zero included) counts as zero there: the products q.k drop
+  // out (Q is zeroed) and the scores are the bias alone, kscale = 1.
+  const bool q_dropped = ALIBI && !(scale >= 0x1p-64f);
+  const float kscale = !ALIBI ? scale : (q_dropped ? 1.f : scale);
+  const float sigma = ALIBI ? slopes[hq] / kscale : 0.f;
 
   bf16x8 qf[D / 16];
   {
-    const bool ok = my_row < Sq;
+    const bool ok = my_row < Sq && !q_dropped;
     const uint16_t* qrow = Q + (q_head + (size_t)(ok ? my_row : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
@@ -365,11 +374,9 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
   float l_run = 0.f;
   // exp2 argument scale, scale*log2(e), kept >= the smallest normal float: a
   // zero (or tiny) scale then still gives every visible key p = exp2(~0) = 1
-  // exactly, as scale = 0 does, while masked -inf scores keep p = 0.
-  //
-  // EXT works in scaled units instead: the kernel adds the bias to
-  // scale * s and exponentiates with c = log2(e).
-  const float c = EXT ? kLog2e : fmaxf(scale * kLog2e, 1.17549435e-38f);
+  // exactly, as scale = 0 does, while masked -inf scores keep p = 0.  With
+  // the bias, kscale >= 2^-64 already.
+  const float c = ALIBI ? kscale * kLog2e : fmaxf(scale * kLog2e, 1.17549435e-38f);
 
   constexpr int kN = 2 * (D / 16);  // MFMAs of each product per tile
   static_assert(kN == 4 * (D / 32), "both products take the same number of MFMAs");
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
       if (WITH_S)
-        s[i & 1] = mfma16<IS_F16>(kring[i % kP], qf[i >> 1], i < 2 ? f32x16{} : s[i & 1]);
+        s[i & 1] = mfma16<IS_F16>(kring[i % kP], qf[i >> 1], (i < 2 && !ALIBI) ? f32x16{} : s[i & 1]);
       if (WITH_PV) {
         const int g = i / (D / 32), db = i % (D / 32);
         acc[db] = mfma16<IS_F16>(vring[i % kP], pf[g >> 1][g & 1], acc[db]);
@@ -411,7 +418,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     using FF_ = std::false_type;
     constexpr bool WITH_S = decltype(with_s_c)::value;
     constexpr bool WITH_PV = decltype(with_pv_c)::value;
-    if constexpr (!EXT) {
+    if constexpr (!MASK) {
       matrix_body(with_s_c, with_pv_c, j);
     } else {
       // Two independent products, one after the other, each behind its own
@@ -421,40 +428,45 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     }
   };
 
-  // Vector phase: mask tile j where needed, online softmax, pack P_j.
+  // Bias of tile j in units of 1/kscale, written into s as the starting value
+  // of the S product: key - row = d, bias = slope * d (causal: every visible
+  // d <= 0) or -slope * |d| (non-causal).  One FMA per score when causal.
+  auto bias_init = [&](int j) {
+    const float d0 = (float)(tile(j) * kBlockN + 4 * half - my_row);
+    const float b0 = sigma * d0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float kr = (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
+        s[kb][r] = CAUSAL ? fmaf(sigma, kr, b0) : -sigma * fabsf(d0 + kr);
+      }
+  };
+
+  // Vector phase: mask tile j where needed, online softmax, pack P_j; with
+  // the bias, then the starting value of S_{j+1}.
   // Tiles past a causal wave's diagonal come out fully masked (p = 0): the
   // tile max is -inf, the reference max stays, and acc and l are unchanged.
+  // With a block mask, a tile this wave cannot see changes nothing (its
+  // matrix phases skip it too).
   auto vector_phase = [&](int j) {
-    // Block mask: a tile this wave cannot see changes nothing (its matrix
-    // phases skip it too).
-    if (EXT && !wave_sees(j)) return;
-    const int key0 = tile(j) * kBlockN;
-    if constexpr (EXT) {
-      // Scaled score plus the linear bias: key - row = d, bias = slope * d
-      // (causal: every visible d <= 0) or -slope * |d| (non-causal).
-      const float d0 = (float)(key0 + 4 * half - my_row);
+    if (!MASK || wave_sees(j)) {
+      const int key0 = tile(j) * kBlockN;
+      const bool need_mask = (CAUSAL && key0 + kBlockN - 1 > qw) || (key0 + kBlockN > Sk);
+      if (need_mask) {
+        const int lim = (CAUSAL ? min(Sk - 1, my_row) : Sk - 1) - key0 - 4 * half;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float d = d0 + (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
-          const float bias = CAUSAL ? slope * d : -slope * fabsf(d);
-          s[kb][r] = fmaf(s[kb][r], scale, bias);
-        }
+          for (int r = 0; r < 16; ++r)
+            s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) <= lim) ? s[kb][r] : -INFINITY;
+      }
+      // c > 0 here, so a masked (-inf) score gives p = exp2(-inf) = 0 without
+      // a separate masked code path.
+      softmax_tile<IS_F16, MASK>(s, m_run, l_run, c, acc, pf);
     }
-    const bool sees = wave_sees(j);
-    const bool need_mask = (CAUSAL && key0 + kBlockN - 1 > qw) || (key0 + kBlockN > Sk) || !sees;
-    if (need_mask) {
-      const int lim = !sees ? -kBlockN : (CAUSAL ? min(Sk - 1, my_row) : Sk - 1) - key0 - 4 * half;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) <= lim) ? s[kb][r] : -INFINITY;
-    }
-    // c > 0 here, so a masked (-inf) score gives p = exp2(-inf) = 0 without
-    // a separate masked code path.
-    softmax_tile<IS_F16, EXT>(s, m_run, l_run, c, acc, pf);
+    if constexpr (ALIBI)
+      if (j + 1 < nt) bias_init(j + 1);
   };
 
   using TT = std::true_type;
@@ -493,7 +505,8 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
 
   // A workgroup whose block mask shows it no tile skips the loop: its rows
   // have no visible key (o = 0, lse = -inf below).
-  if (!EXT || nt > 0) {
+  if (!MASK || nt > 0) {
+    if constexpr (ALIBI) bias_init(0);
     load_rows(krsrc, tile(0), kreg);
     store_rows(kslot(0), T::kKPitch, kreg);
     if (group == 1) {
@@ -517,8 +530,9 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
 
   // ---- epilogue: O = acc / l, lse = m*scale + ln l --------------------------
   const float l_tot = wave_pair_sum(l_run);
-  // EXT: a row with no visible key (l = 0, m = -inf) gets o = 0, lse = -inf.
-  const float inv = (EXT && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
+  // Block mask: a row with no visible key (l = 0, m = -inf) gets o = 0,
+  // lse = -inf.
+  const float inv = (MASK && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
   if (my_row < Sq) {
     uint16_t* orow = O + (q_head + my_row) * D;
 #pragma unroll
@@ -535,7 +549,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
               ((uint32_t)__builtin_bit_cast(uint16_t, o4[3]) << 16);
         *reinterpret_cast<uint2*>(orow + db * 32 + 8 * g + 4 * half) = u;
       }
-    if (half == 0) LSE[q_head + my_row] = m_run * (EXT ? 1.f : scale) + logf(l_tot);
+    if (half == 0) LSE[q_head + my_row] = m_run * kscale + logf(l_tot);
   }
 }
 
@@ -735,30 +749,43 @@ int launch16(Kern kernel, const uint16_t* q, const uint16_t* k, const uint16_t* 
   return e == hipSuccess ? TILEATTN_OK : TILEATTN_ERR_LAUNCH;
 }
 
-// bf16 and fp16 inputs share one kernel template (IS_F16); EXT adds the
-// linear bias and the block mask.
-template <bool IS_F16, bool EXT>
+// bf16 and fp16 inputs share one kernel template (IS_F16); a block mask and
+// the linear bias select the MASK / ALIBI instances.
+template <int D, bool IS_F16, bool MASK, bool ALIBI>
+int launch_variant(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                   int B, int Hq, int Hkv, int Sq, int Sk, float scale, int causal,
+                   const float* slopes, const unsigned char* bmask, int mask_heads, void* stream) {
+  using T = Bf16Tile<D>;
+  return causal ? launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, true, IS_F16, MASK, ALIBI>, q, k,
+                                                    v, o, lse, B, Hq, Hkv, Sq, Sk, scale, slopes, bmask,
+                                                    mask_heads, stream)
+                : launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, false, IS_F16, MASK, ALIBI>, q, k,
+                                                    v, o, lse, B, Hq, Hkv, Sq, Sk, scale, slopes, bmask,
+                                                    mask_heads, stream);
+}
+
+template <bool IS_F16>
 int fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
           int Hkv, int Sq, int Sk, int D, float scale, int causal, const float* slopes,
           const unsigned char* bmask, int mask_heads, void* stream) {
   bool empty;
   const int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty);
   if (st != TILEATTN_OK) return st;
-  if (EXT) {
-    if (bmask != nullptr && mask_heads != 1 && mask_heads != Hq) return TILEATTN_ERR_BAD_SHAPE;
-    if (bmask != nullptr && Sk > 64 * kMaxMaskedTiles) return TILEATTN_ERR_TOO_LARGE;
-    if (slopes != nullptr && (reinterpret_cast<uintptr_t>(slopes) & 3u) != 0) return TILEATTN_ERR_ALIGNMENT;
-  }
+  if (bmask != nullptr && mask_heads != 1 && mask_heads != Hq) return TILEATTN_ERR_BAD_SHAPE;
+  if (bmask != nullptr && Sk > 64 * kMaxMaskedTiles) return TILEATTN_ERR_TOO_LARGE;
+  if (slopes != nullptr && (reinterpret_cast<uintptr_t>(slopes) & 3u) != 0) return TILEATTN_ERR_ALIGNMENT;
   if (empty) return TILEATTN_OK;
   auto qq = static_cast<const uint16_t*>(q), kk = static_cast<const uint16_t*>(k),
        vv = static_cast<const uint16_t*>(v);
   auto oo = static_cast<uint16_t*>(o);
-#define TILEATTN_L16(DD, CC) launch16<Bf16Tile<DD>::kBlockM, Bf16Tile<DD>::kThreads>(               \
-      attn_fwd_16_kernel<DD, CC, IS_F16, EXT>, qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, \
-      slopes, bmask, mask_heads, stream)
-  if (D == 128) return causal ? TILEATTN_L16(128, true) : TILEATTN_L16(128, false);
-  return causal ? TILEATTN_L16(64, true) : TILEATTN_L16(64, false);
-#undef TILEATTN_L16
+#define TILEATTN_V16(MM, AA)                                                                        \
+  (D == 128 ? launch_variant<128, IS_F16, MM, AA>(qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale,  \
+                                                  causal, slopes, bmask, mask_heads, stream)       \
+            : launch_variant<64, IS_F16, MM, AA>(qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale,   \
+                                                 causal, slopes, bmask, mask_heads, stream))
+  if (bmask != nullptr) return slopes != nullptr ? TILEATTN_V16(true, true) : TILEATTN_V16(true, false);
+  return slopes != nullptr ? TILEATTN_V16(false, true) : TILEATTN_V16(false, false);
+#undef TILEATTN_V16
 }
 
 }  // namespace
@@ -766,15 +793,13 @@ int fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int 
 extern "C" int tileattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
                             int causal, void* stream) {
-  return fwd16<false, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, nullptr, nullptr, 1,
-                             stream);
+  return fwd16<false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, nullptr, nullptr, 1, stream);
 }
 
 extern "C" int tileattn_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
                                 int causal, void* stream) {
-  return fwd16<true, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, nullptr, nullptr, 1,
-                            stream);
+  return fwd16<true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, nullptr, nullptr, 1, stream);
 }
 
 extern "C" int tileattn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -782,10 +807,10 @@ extern "C" int tileattn_fwd_ext(const void* q, const void* k, const void* v, voi
                                 int causal, const float* alibi_slopes,
                                 const unsigned char* block_mask, int mask_heads, int is_f16,
                                 void* stream) {
-  return is_f16 ? fwd16<true, true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal,
-                                    alibi_slopes, block_mask, mask_heads, stream)
-                : fwd16<false, true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal,
-                                     alibi_slopes, block_mask, mask_heads, stream);
+  return is_f16 ? fwd16<true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, alibi_slopes,
+                              block_mask, mask_heads, stream)
+                : fwd16<false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, alibi_slopes,
+                               block_mask, mask_heads, stream);
 }
 
 extern "C" int tileattn_fwd_f32(const float* q, const float* k, const float* v, float* o,

@@ -23,7 +23,7 @@ import json
 import os
 import statistics
 
-KERNEL_KEY = "attn_fwd_16_kernel<128, true, false, false>"
+KERNEL_KEY = "attn_fwd_16_kernel<128, true, false, false, false>"
 COPY_BYTES = 256 * 1024 * 1024
 SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "tileattn.hip")
 
