@@ -1,6 +1,6 @@
 """Benchmark: attention forward TFLOP/s on the causal GQA 8K workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--no-cpu] [--only matmul]
 
 One step = one launch of the whole hot path (``tileattn_fwd``) on the
 causal grouped-query workload B=1, Hq=32, Hkv=8, Sq=Sk=8192, D=128, bf16,
@@ -14,6 +14,10 @@ kernel's duration taken from HIP events recorded on the launch stream.
 The CPU baseline is the fp64 oracle run on the same workload on the host's
 cores.  ``traffic`` is the kernel's HBM bytes per launch from the committed
 rocprofv3 counter summary in profiles/ (null when the kernel changed since).
+
+``--all`` also times, on stderr, the bf16 matrix product (tileattn_matmul),
+the other attention workloads and the biased / block-masked variants;
+``--only matmul`` times the matrix product alone and prints no JSON line.
 """
 
 from __future__ import annotations
@@ -115,6 +119,42 @@ def time_ext(ta, w, steps, warmup, mask, alibi=True):
     return t, 4.0 * w.B * w.D * pairs
 
 
+def time_events(fn, steps, warmup):
+    """Median and mean of ``steps`` launches of fn, HIP events on the current stream."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return float(np.median(ms)) * 1e-3, float(np.mean(ms)) * 1e-3
+
+
+def matmul_lines(ta, steps, warmup):
+    """Time the bf16 matrix product (fp32 and bf16 C) and, for context, the
+    library GEMM torch.matmul dispatches to on the same inputs."""
+    from tiled_attention_tileattn_amd.inputs import MATMUL_WORKLOADS, random_matrices
+
+    for name, (M, N, K, seed) in MATMUL_WORKLOADS.items():
+        a, b = random_matrices(M, N, K, seed, device="cuda")
+        flop = 2.0 * M * N * K
+        for dt, dname in ((torch.float32, "fp32"), (torch.bfloat16, "bf16")):
+            c = torch.empty((M, N), dtype=dt, device="cuda")
+            med, mean = time_events(lambda: ta.matmul(a, b, out=c), steps, warmup)
+            log(f"{name} (M=N=K={M}, C {dname}): median {med*1e6:.1f} us mean {mean*1e6:.1f} us "
+                f"-> {flop/med/1e12:.1f} TFLOP/s ({flop/med/1e12/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        med, _ = time_events(lambda: torch.matmul(a, b, out=c), steps, warmup)
+        log(f"{name}: torch.matmul (ROCm library GEMM, C bf16, context only): median {med*1e6:.1f} us "
+            f"-> {flop/med/1e12:.1f} TFLOP/s")
+        del a, b, c
+
+
 def cpu_baseline(w):
     """Time the fp64 oracle on the whole workload on this host's cores.
 
@@ -169,6 +209,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["matmul"], help="time only that kernel (stderr) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -195,7 +236,12 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
 
+    if args.only == "matmul":
+        matmul_lines(ta, args.steps, args.warmup)
+        return
+
     if args.all:
+        matmul_lines(ta, args.steps, args.warmup)
         for name, w in WORKLOADS.items():
             if name == HEADLINE:
                 continue

@@ -51,7 +51,8 @@ extern "C" {
 typedef enum {
   TILEATTN_OK = 0,
   TILEATTN_ERR_NULL_POINTER = -1, /* q, k, v, o or lse is NULL (non-empty problem)   */
-  TILEATTN_ERR_BAD_SHAPE = -2,    /* a size < 0, or Hkv < 1 or Sk < 1                 */
+  TILEATTN_ERR_BAD_SHAPE = -2,    /* a size < 0; attention: Hkv < 1 or Sk < 1;         */
+                                  /* matmul: N or K not a multiple of 8               */
   TILEATTN_ERR_GQA_RATIO = -3,    /* Hq is not a multiple of Hkv                      */
   TILEATTN_ERR_HEAD_DIM = -4,     /* D is not 64 or 128                               */
   TILEATTN_ERR_SCALE = -5,        /* scale is negative, NaN or infinite               */
@@ -134,6 +135,27 @@ int tileattn_fwd_ext(const void* q, const void* k, const void* v, void* o, float
 int tileattn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                      int B, int Hq, int Hkv, int Sq, int Sk, int D,
                      float scale, int causal, void* stream);
+
+/*
+ * Tiled matrix product C = A * B with bf16 inputs and an fp32 accumulator:
+ * the first page's step 5 (Passo a Passo, "Multiplicacao de Matrizes
+ * Tiled"): per output tile, an fp32 accumulator adds the products of A and B
+ * blocks over the K loop; its Troubleshooting section explains why the
+ * accumulator must be fp32 even for 16-bit inputs.
+ *   a : bf16 [M, K] row-major, device pointer, 16-byte aligned.
+ *   b : bf16 [K, N] row-major, device pointer, 16-byte aligned.
+ *   c : [M, N] row-major output, fp32 (out_bf16 = 0: the accumulator as it
+ *       is) or bf16 (out_bf16 != 0: rounded to nearest even), 16-byte aligned.
+ *   M >= 0; N and K >= 0 and multiples of 8.  M or N = 0 launches nothing;
+ *   K = 0 writes zeros (a and b are not read and may be NULL).  The caller owns every buffer; nothing is allocated.
+ *   stream : hipStream_t to launch on, NULL for the default stream.
+ * Errors: TILEATTN_ERR_BAD_SHAPE (negative size, N or K not a multiple of 8),
+ * TILEATTN_ERR_NULL_POINTER, TILEATTN_ERR_ALIGNMENT, TILEATTN_ERR_TOO_LARGE
+ * (512*K or 128*N bytes above 2^31-1: 32-bit offsets within one tile),
+ * TILEATTN_ERR_LAUNCH.
+ */
+int tileattn_matmul(const void* a, const void* b, void* c, int M, int N, int K, int out_bf16,
+                    void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* tileattn_strerror(int status);

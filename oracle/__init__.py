@@ -32,14 +32,20 @@ Modules:
   mask (features the first page's FAQ names for the official library);
   the readings are in its docstring.
 * ``brute``     — pure-Python triple loop with ``math.fsum``; tiny inputs only.
+* ``matmul``    — the plain matrix product C = A B in float64, which the tiled
+  fp32-accumulating K loop of the first page's step 5 ("Multiplicação de
+  Matrizes Tiled") computes block by block.
 
 Every function here is pinned by ``-m "not gpu"`` tests against facts that
 do not come from the oracle itself (closed forms, invariants, a library
-routine, brute force); see ``tests/test_oracle_pins.py``.
+routine, brute force); see ``tests/test_oracle_pins.py``,
+``tests/test_oracle_ext_pins.py`` and ``tests/test_oracle_matmul_pins.py``.
 """
 
 from .full_softmax import attention, attention_rows, visible_count
 from .biased import attention_ext
 from .brute import attention_bruteforce
+from .matmul import matmul, matmul_rows
 
-__all__ = ["attention", "attention_rows", "visible_count", "attention_ext", "attention_bruteforce"]
+__all__ = ["attention", "attention_rows", "visible_count", "attention_ext", "attention_bruteforce",
+           "matmul", "matmul_rows"]

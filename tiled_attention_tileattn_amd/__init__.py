@@ -1,7 +1,8 @@
 """tileattn: exact attention forward for MI355X (gfx950), HIP kernels behind a C ABI.
 
-``forward(q, k, v, causal, scale) -> (o, lse)`` is the torch-facing entry;
-``tileattn_fwd`` / ``tileattn_fwd_f16`` / ``tileattn_fwd_ext`` / ``tileattn_fwd_f32`` /
+``forward(q, k, v, causal, scale) -> (o, lse)`` and ``matmul(a, b) -> c`` are
+the torch-facing entries; ``tileattn_fwd`` / ``tileattn_fwd_f16`` /
+``tileattn_fwd_ext`` / ``tileattn_fwd_f32`` / ``tileattn_matmul`` /
 ``tileattn_strerror`` /
 ``tileattn_launch_shape`` mirror the C functions of ``include/tileattn.h``.
 The shared library is loaded on first use and must have been built
@@ -14,10 +15,12 @@ from .binding import (  # noqa: F401
     TileAttnError,
     forward,
     load_library,
+    matmul,
     tileattn_fwd,
     tileattn_fwd_ext,
     tileattn_fwd_f16,
     tileattn_fwd_f32,
     tileattn_launch_shape,
+    tileattn_matmul,
     tileattn_strerror,
 )

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtileattn.so")
 
 EXPORTED = ("tileattn_fwd", "tileattn_fwd_f16", "tileattn_fwd_ext", "tileattn_fwd_f32",
-            "tileattn_strerror", "tileattn_launch_shape")
+            "tileattn_matmul", "tileattn_strerror", "tileattn_launch_shape")
 
 STATUS = {
     0: "TILEATTN_OK",
@@ -61,6 +61,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tileattn_fwd_ext.restype = i
     lib.tileattn_fwd_f32.argtypes = sig
     lib.tileattn_fwd_f32.restype = i
+    lib.tileattn_matmul.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    lib.tileattn_matmul.restype = i
     lib.tileattn_strerror.argtypes = [i]
     lib.tileattn_strerror.restype = ctypes.c_char_p
     lib.tileattn_launch_shape.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i),
@@ -90,6 +92,10 @@ def tileattn_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, alib
 def tileattn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream) -> int:
     return load_library().tileattn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D,
                                            float(scale), int(bool(causal)), stream)
+
+
+def tileattn_matmul(a, b, c, M, N, K, out_bf16, stream) -> int:
+    return load_library().tileattn_matmul(a, b, c, M, N, K, int(bool(out_bf16)), stream)
 
 
 def tileattn_strerror(status: int) -> str:
@@ -181,3 +187,43 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     if rc != 0:
         raise TileAttnError(rc, fn.__name__)
     return out, lse
+
+
+def matmul(a, b, out=None, out_dtype=None, stream=None):
+    """C = A @ B on the GPU with an fp32 accumulator: returns C.
+
+    a [M, K] and b [K, N]: contiguous bfloat16 tensors on one HIP device, N
+    and K multiples of 8.  ``out_dtype`` is torch.float32 (default: the
+    accumulator as it is) or torch.bfloat16; ``out`` may be preallocated
+    ([M, N], contiguous, that dtype).  ``stream`` is a torch stream (default:
+    the current stream of a's device).
+    """
+    import torch
+
+    for name, t in (("a", a), ("b", b)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2 or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a 2-D bfloat16 torch tensor")
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor on a HIP device")
+    if a.device != b.device:
+        raise ValueError("a and b must be on the same device")
+    M, K = a.shape
+    Kb, N = b.shape
+    if Kb != K:
+        raise ValueError(f"shape mismatch a{tuple(a.shape)} b{tuple(b.shape)}")
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    if tuple(out.shape) != (M, N) or out.dtype != out_dtype or not out.is_contiguous() \
+            or out.device != a.device:
+        raise ValueError(f"out must be a contiguous {out_dtype} tensor [{M}, {N}] on a's device")
+    with torch.cuda.device(a.device):
+        s = stream if stream is not None else torch.cuda.current_stream(a.device)
+        rc = tileattn_matmul(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
+                             out_dtype == torch.bfloat16, s.cuda_stream)
+    if rc != 0:
+        raise TileAttnError(rc, "tileattn_matmul")
+    return out

@@ -702,6 +702,8 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
   if (Hq % Hkv != 0) return TILEATTN_ERR_GQA_RATIO;
   if (D != 64 && D != 128) return TILEATTN_ERR_HEAD_DIM;
   if (!(scale >= 0.f) || isinf(scale)) return TILEATTN_ERR_SCALE;
+  // Row indices inside the kernels stay within int: Sq <= 2^30.
+  if (Sq > (1 << 30)) return TILEATTN_ERR_TOO_LARGE;
   // 64-bit index range: elements of q/o and of k/v, and the workgroup count.
   const double q_elems = (double)B * Hq * Sq * D;
   const double kv_elems = (double)B * Hkv * Sk * D;
@@ -830,7 +832,7 @@ extern "C" const char* tileattn_strerror(int status) {
   switch (status) {
     case TILEATTN_OK: return "ok";
     case TILEATTN_ERR_NULL_POINTER: return "a tensor pointer is NULL";
-    case TILEATTN_ERR_BAD_SHAPE: return "bad shape: sizes must be >= 0, Hkv >= 1 and Sk >= 1";
+    case TILEATTN_ERR_BAD_SHAPE: return "bad shape: sizes must be >= 0 (attention: Hkv, Sk >= 1; matmul: N, K multiples of 8)";
     case TILEATTN_ERR_GQA_RATIO: return "Hq must be a multiple of Hkv";
     case TILEATTN_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";
     case TILEATTN_ERR_SCALE: return "scale must be finite and >= 0";

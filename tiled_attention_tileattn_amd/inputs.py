@@ -139,3 +139,29 @@ def window_block_mask(Sq: int, Sk: int, window_blocks: int, block: int = 64) -> 
         m[0, qb, max(0, qb - window_blocks + 1): min(nk, qb + 1)] = 1
         m[0, qb, 0] = 1
     return torch.from_numpy(m).contiguous()
+
+
+# ---- matrix product inputs ---------------------------------------------------
+# name -> (M, N, K, seed): the square bf16 product timed next to the attention.
+MATMUL_WORKLOADS = {
+    "matmul_bf16_8k": (8192, 8192, 8192, 11),
+}
+
+
+def random_matrices(M: int, N: int, K: int, seed: int, integer: bool = False,
+                    device: str | torch.device = "cpu"):
+    """Seeded bf16 A [M, K] and B [K, N] for the matrix product.
+
+    Draws from torch.Generator('cpu').manual_seed(seed), A first and then B:
+    N(0, 1) float32 values cast to bf16 (round to nearest even), or with
+    ``integer`` integers uniform in [-4, 4] (exact in bf16; every product and
+    every partial sum of up to 2^19 of them is then exact in fp32).
+    """
+    g = torch.Generator("cpu").manual_seed(seed)
+    if integer:
+        a = torch.randint(-4, 5, (M, K), generator=g, dtype=torch.int32).to(torch.float32)
+        b = torch.randint(-4, 5, (K, N), generator=g, dtype=torch.int32).to(torch.float32)
+    else:
+        a = torch.randn((M, K), generator=g, dtype=torch.float32)
+        b = torch.randn((K, N), generator=g, dtype=torch.float32)
+    return a.to(torch.bfloat16).to(device).contiguous(), b.to(torch.bfloat16).to(device).contiguous()
