@@ -16,8 +16,9 @@ cores.  ``traffic`` is the kernel's HBM bytes per launch from the committed
 rocprofv3 counter summary in profiles/ (null when the kernel changed since).
 
 ``--all`` also times, on stderr, the bf16 matrix product (tileattn_matmul),
-the other attention workloads and the biased / block-masked variants;
-``--only matmul`` times the matrix product alone and prints no JSON line.
+the row softmax and fused GELU (GB/s against the 8 TB/s HBM peak), the other
+attention workloads and the biased / block-masked variants; ``--only matmul``
+or ``--only rowwise`` times just those and prints no JSON line.
 """
 
 from __future__ import annotations
@@ -155,6 +156,44 @@ def matmul_lines(ta, steps, warmup):
         del a, b, c
 
 
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+
+def rowwise_lines(ta, steps, warmup):
+    """Time the row softmax and the fused GELU: algorithmic bytes (inputs read
+    once, output written once) per launch over the launch time, in GB/s."""
+    from tiled_attention_tileattn_amd.inputs import ROWWISE_WORKLOADS, random_gelu_inputs, random_rows
+
+    for name, (kind, dtype, shape, seed) in ROWWISE_WORKLOADS.items():
+        esize = 4 if dtype == "fp32" else 2
+        if kind == "softmax":
+            x = random_rows(*shape, seed=seed, dtype=dtype, device="cuda")
+            out = torch.empty_like(x)
+            nbytes = 2.0 * x.numel() * esize
+            med, mean = time_events(lambda: ta.softmax(x, out=out), steps, warmup)
+            bufs = (x, out)
+        else:
+            x, w, b = random_gelu_inputs(shape[0], seed=seed, dtype=dtype, device="cuda")
+            out = torch.empty_like(x)
+            nbytes = 4.0 * x.numel() * esize
+            med, mean = time_events(lambda: ta.gelu(x, w, b, out=out), steps, warmup)
+            bufs = (x, w, b, out)
+        log(f"{name}: median {med*1e6:.1f} us mean {mean*1e6:.1f} us -> {nbytes/med/1e9:.0f} GB/s "
+            f"({nbytes/med/1e9/PEAK_HBM_GBS*100:.1f}% of HBM peak; {nbytes/2**30:.2f} GiB per launch)")
+        if kind == "softmax":
+            med, _ = time_events(lambda: torch.softmax(x, dim=1, out=out), steps, warmup)
+            log(f"{name}: torch.softmax (context only): median {med*1e6:.1f} us -> {nbytes/med/1e9:.0f} GB/s")
+        del bufs, x, out
+    # What a plain streaming copy reaches on this device (context for the rates above).
+    src = torch.empty(1 << 29, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    med, _ = time_events(lambda: dst.copy_(src), steps, warmup)
+    nbytes = 2.0 * src.numel() * 4
+    log(f"device copy 2 GiB -> 2 GiB (torch copy_, context only): median {med*1e6:.1f} us -> "
+        f"{nbytes/med/1e9:.0f} GB/s ({nbytes/med/1e9/PEAK_HBM_GBS*100:.1f}% of HBM peak)")
+    del src, dst
+
+
 def cpu_baseline(w):
     """Time the fp64 oracle on the whole workload on this host's cores.
 
@@ -209,7 +248,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["matmul"], help="time only that kernel (stderr) and exit")
+    ap.add_argument("--only", choices=["matmul", "rowwise"],
+                    help="time only those kernels (stderr) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -239,9 +279,13 @@ def main():
     if args.only == "matmul":
         matmul_lines(ta, args.steps, args.warmup)
         return
+    if args.only == "rowwise":
+        rowwise_lines(ta, args.steps, args.warmup)
+        return
 
     if args.all:
         matmul_lines(ta, args.steps, args.warmup)
+        rowwise_lines(ta, args.steps, args.warmup)
         for name, w in WORKLOADS.items():
             if name == HEADLINE:
                 continue

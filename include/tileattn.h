@@ -60,8 +60,15 @@ typedef enum {
   TILEATTN_ERR_TOO_LARGE = -7,    /* a size product exceeds the 64-bit index range,   */
                                   /* or Sk*D*4 > 2^31-1 (one head's K or V is read    */
                                   /* with 32-bit buffer offsets)                      */
-  TILEATTN_ERR_LAUNCH = -8        /* the HIP launch failed (e.g. no gfx950 device)    */
+  TILEATTN_ERR_LAUNCH = -8,       /* the HIP launch failed (e.g. no gfx950 device)    */
+  TILEATTN_ERR_DTYPE = -9         /* unknown tileattn_dtype code                      */
 } tileattn_status;
+
+/* Storage type codes of tileattn_softmax and tileattn_gelu. */
+typedef enum {
+  TILEATTN_DTYPE_F32 = 0,         /* IEEE binary32                                    */
+  TILEATTN_DTYPE_BF16 = 1         /* bfloat16; results rounded to nearest even        */
+} tileattn_dtype;
 
 /*
  * bfloat16 attention forward (the hot path).
@@ -156,6 +163,38 @@ int tileattn_fwd_f32(const float* q, const float* k, const float* v, float* o, f
  */
 int tileattn_matmul(const void* a, const void* b, void* c, int M, int N, int K, int out_bf16,
                     void* stream);
+
+/*
+ * Row softmax: the first page's step 4 (Passo a Passo, "Softmax por Linha"):
+ * per row, subtract the row maximum, exponentiate, divide by the sum of the
+ * exponentials (the max subtraction keeps the largest term at 1).
+ *   out[r, c] = exp(x[r, c] - max_c' x[r, c']) / sum_c'' exp(x[r, c''] - max)
+ * for r < n_rows, c < n_cols; element (r, c) of x and out is at r*stride + c.
+ *   x, out : device pointers, 16-byte aligned, dtype (tileattn_dtype) storage;
+ *            out may be x (in place).  Arithmetic is fp32.
+ *   n_rows >= 0 (0: nothing is launched), 1 <= n_cols <= stride, stride a
+ *   multiple of 16 bytes.  A row whose entries are all -inf gives NaN, as
+ *   the definition does (-inf - -inf).
+ * Errors: TILEATTN_ERR_DTYPE, TILEATTN_ERR_BAD_SHAPE, TILEATTN_ERR_ALIGNMENT
+ * (pointer or stride), TILEATTN_ERR_NULL_POINTER, TILEATTN_ERR_TOO_LARGE,
+ * TILEATTN_ERR_LAUNCH.
+ */
+int tileattn_softmax(const void* x, void* out, int n_rows, int n_cols, long long stride, int dtype,
+                     void* stream);
+
+/*
+ * Fused GELU: the first page's step 3 (Passo a Passo, "GELU Fundido"): one
+ * pass computes h = x*w + b elementwise and the tanh approximation of GELU,
+ *   out[i] = 0.5 h (1 + tanh(sqrt(2/pi) (h + 0.044715 h^3))),  h = x[i]*w[i] + b[i],
+ * for i < n (x, w, b, out all of n elements).  Arithmetic is fp32.
+ *   x, w, b, out : device pointers, 16-byte aligned, dtype storage; out may be
+ *                  one of the inputs.  n >= 0 (0: nothing is launched).
+ * Errors: TILEATTN_ERR_DTYPE, TILEATTN_ERR_BAD_SHAPE (n < 0),
+ * TILEATTN_ERR_NULL_POINTER, TILEATTN_ERR_ALIGNMENT, TILEATTN_ERR_TOO_LARGE,
+ * TILEATTN_ERR_LAUNCH.
+ */
+int tileattn_gelu(const void* x, const void* w, const void* b, void* out, long long n, int dtype,
+                  void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* tileattn_strerror(int status);

@@ -35,17 +35,21 @@ Modules:
 * ``matmul``    — the plain matrix product C = A B in float64, which the tiled
   fp32-accumulating K loop of the first page's step 5 ("Multiplicação de
   Matrizes Tiled") computes block by block.
+* ``rowwise``   — the row softmax (step 4 "Softmax por Linha") and the fused
+  GELU (step 3 "GELU Fundido") of the same page, in float64.
 
 Every function here is pinned by ``-m "not gpu"`` tests against facts that
 do not come from the oracle itself (closed forms, invariants, a library
 routine, brute force); see ``tests/test_oracle_pins.py``,
-``tests/test_oracle_ext_pins.py`` and ``tests/test_oracle_matmul_pins.py``.
+``tests/test_oracle_ext_pins.py``, ``tests/test_oracle_matmul_pins.py`` and
+``tests/test_oracle_rowwise_pins.py``.
 """
 
 from .full_softmax import attention, attention_rows, visible_count
 from .biased import attention_ext
 from .brute import attention_bruteforce
 from .matmul import matmul, matmul_rows
+from .rowwise import gelu_fused, softmax_rows
 
 __all__ = ["attention", "attention_rows", "visible_count", "attention_ext", "attention_bruteforce",
-           "matmul", "matmul_rows"]
+           "matmul", "matmul_rows", "softmax_rows", "gelu_fused"]

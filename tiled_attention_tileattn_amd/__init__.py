@@ -1,9 +1,10 @@
 """tileattn: exact attention forward for MI355X (gfx950), HIP kernels behind a C ABI.
 
-``forward(q, k, v, causal, scale) -> (o, lse)`` and ``matmul(a, b) -> c`` are
-the torch-facing entries; ``tileattn_fwd`` / ``tileattn_fwd_f16`` /
-``tileattn_fwd_ext`` / ``tileattn_fwd_f32`` / ``tileattn_matmul`` /
-``tileattn_strerror`` /
+``forward(q, k, v, causal, scale) -> (o, lse)``, ``matmul(a, b) -> c``,
+``softmax(x) -> out`` and ``gelu(x, w, b) -> out`` are the torch-facing
+entries; ``tileattn_fwd`` / ``tileattn_fwd_f16`` / ``tileattn_fwd_ext`` /
+``tileattn_fwd_f32`` / ``tileattn_matmul`` / ``tileattn_softmax`` /
+``tileattn_gelu`` / ``tileattn_strerror`` /
 ``tileattn_launch_shape`` mirror the C functions of ``include/tileattn.h``.
 The shared library is loaded on first use and must have been built
 (``python -m tiled_attention_tileattn_amd.build``); there is no fallback.
@@ -14,13 +15,17 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     TileAttnError,
     forward,
+    gelu,
     load_library,
     matmul,
+    softmax,
     tileattn_fwd,
     tileattn_fwd_ext,
     tileattn_fwd_f16,
     tileattn_fwd_f32,
+    tileattn_gelu,
     tileattn_launch_shape,
     tileattn_matmul,
+    tileattn_softmax,
     tileattn_strerror,
 )

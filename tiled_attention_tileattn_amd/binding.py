@@ -18,7 +18,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtileattn.so")
 
 EXPORTED = ("tileattn_fwd", "tileattn_fwd_f16", "tileattn_fwd_ext", "tileattn_fwd_f32",
-            "tileattn_matmul", "tileattn_strerror", "tileattn_launch_shape")
+            "tileattn_matmul", "tileattn_softmax", "tileattn_gelu", "tileattn_strerror",
+            "tileattn_launch_shape")
+
+DTYPE_F32, DTYPE_BF16 = 0, 1  # tileattn_dtype codes
 
 STATUS = {
     0: "TILEATTN_OK",
@@ -30,6 +33,7 @@ STATUS = {
     -6: "TILEATTN_ERR_ALIGNMENT",
     -7: "TILEATTN_ERR_TOO_LARGE",
     -8: "TILEATTN_ERR_LAUNCH",
+    -9: "TILEATTN_ERR_DTYPE",
 }
 
 _lib = None
@@ -63,6 +67,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tileattn_fwd_f32.restype = i
     lib.tileattn_matmul.argtypes = [vp, vp, vp, i, i, i, i, vp]
     lib.tileattn_matmul.restype = i
+    ll = ctypes.c_longlong
+    lib.tileattn_softmax.argtypes = [vp, vp, i, i, ll, i, vp]
+    lib.tileattn_softmax.restype = i
+    lib.tileattn_gelu.argtypes = [vp, vp, vp, vp, ll, i, vp]
+    lib.tileattn_gelu.restype = i
     lib.tileattn_strerror.argtypes = [i]
     lib.tileattn_strerror.restype = ctypes.c_char_p
     lib.tileattn_launch_shape.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i),
@@ -96,6 +105,14 @@ def tileattn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stre
 
 def tileattn_matmul(a, b, c, M, N, K, out_bf16, stream) -> int:
     return load_library().tileattn_matmul(a, b, c, M, N, K, int(bool(out_bf16)), stream)
+
+
+def tileattn_softmax(x, out, n_rows, n_cols, stride, dtype, stream) -> int:
+    return load_library().tileattn_softmax(x, out, n_rows, n_cols, stride, dtype, stream)
+
+
+def tileattn_gelu(x, w, b, out, n, dtype, stream) -> int:
+    return load_library().tileattn_gelu(x, w, b, out, n, dtype, stream)
 
 
 def tileattn_strerror(status: int) -> str:
@@ -226,4 +243,68 @@ def matmul(a, b, out=None, out_dtype=None, stream=None):
                              out_dtype == torch.bfloat16, s.cuda_stream)
     if rc != 0:
         raise TileAttnError(rc, "tileattn_matmul")
+    return out
+
+
+def _dtype_code(t):
+    import torch
+
+    codes = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
+    if t.dtype not in codes:
+        raise ValueError("dtype must be torch.float32 or torch.bfloat16")
+    return codes[t.dtype]
+
+
+def softmax(x, out=None, n_cols=None, stream=None):
+    """Row softmax on the GPU: returns out.
+
+    x [n_rows, stride]: a contiguous float32 or bfloat16 tensor on a HIP
+    device; the softmax runs over the first ``n_cols`` columns (default: all)
+    of every row and writes them into ``out`` (same shape and dtype as x; may
+    be x itself).  Columns past n_cols of out are left as they are.
+    """
+    import torch
+
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.device.type != "cuda" or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D tensor on a HIP device")
+    code = _dtype_code(x)
+    n_rows, stride = x.shape
+    n_cols = stride if n_cols is None else int(n_cols)
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous tensor like x")
+    with torch.cuda.device(x.device):
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        rc = tileattn_softmax(x.data_ptr(), out.data_ptr(), n_rows, n_cols, stride, code, s.cuda_stream)
+    if rc != 0:
+        raise TileAttnError(rc, "tileattn_softmax")
+    return out
+
+
+def gelu(x, w, b, out=None, stream=None):
+    """Fused GELU on the GPU: out = gelu_tanh(x * w + b) elementwise; returns out.
+
+    x, w, b: contiguous float32 or bfloat16 tensors of one shape and dtype on
+    one HIP device; ``out`` (same shape and dtype) may be one of them.
+    """
+    import torch
+
+    for name, t in (("x", x), ("w", w), ("b", b)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor on a HIP device")
+    if not (x.shape == w.shape == b.shape) or not (x.dtype == w.dtype == b.dtype) \
+            or not (x.device == w.device == b.device):
+        raise ValueError("x, w, b must share shape, dtype and device")
+    code = _dtype_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous tensor like x")
+    with torch.cuda.device(x.device):
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        rc = tileattn_gelu(x.data_ptr(), w.data_ptr(), b.data_ptr(), out.data_ptr(), x.numel(), code,
+                           s.cuda_stream)
+    if rc != 0:
+        raise TileAttnError(rc, "tileattn_gelu")
     return out

@@ -839,6 +839,7 @@ extern "C" const char* tileattn_strerror(int status) {
     case TILEATTN_ERR_ALIGNMENT: return "tensor pointers must be 16-byte aligned";
     case TILEATTN_ERR_TOO_LARGE: return "problem exceeds the index range";
     case TILEATTN_ERR_LAUNCH: return "kernel launch failed (is a gfx950 device current?)";
+    case TILEATTN_ERR_DTYPE: return "unknown dtype code";
     default: return "unknown tileattn status";
   }
 }

@@ -165,3 +165,42 @@ def random_matrices(M: int, N: int, K: int, seed: int, integer: bool = False,
         a = torch.randn((M, K), generator=g, dtype=torch.float32)
         b = torch.randn((K, N), generator=g, dtype=torch.float32)
     return a.to(torch.bfloat16).to(device).contiguous(), b.to(torch.bfloat16).to(device).contiguous()
+
+
+# ---- row softmax and fused GELU inputs -----------------------------------------
+# name -> (kind, dtype, shape, seed): the memory-bound kernels timed next to
+# the attention (an 8K-column softmax over 64K rows; 2^28-element GELU).
+ROWWISE_WORKLOADS = {
+    "softmax_bf16_64k_x_8k": ("softmax", "bf16", (65536, 8192), 21),
+    "softmax_fp32_64k_x_8k": ("softmax", "fp32", (65536, 8192), 22),
+    "gelu_fp32_256m": ("gelu", "fp32", (1 << 28,), 23),
+    "gelu_bf16_256m": ("gelu", "bf16", (1 << 28,), 24),
+}
+
+
+DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+
+
+def _randn(shape, gen, device, scale, dtype):
+    t = torch.randn(shape, generator=gen, dtype=torch.float32, device=device)
+    if scale != 1.0:
+        t = t * scale
+    return t.to(DTYPES[dtype]).contiguous()
+
+
+def random_rows(n_rows: int, n_cols: int, seed: int, dtype: str = "fp32", scale: float = 1.0,
+                device: str | torch.device = "cpu") -> torch.Tensor:
+    """Seeded [n_rows, n_cols] softmax input: N(0, scale^2) float32 draws from a
+    torch generator on ``device`` seeded with ``seed``, cast to ``dtype``
+    (bf16: round to nearest even).  CPU and GPU draws differ; each is
+    reproducible."""
+    g = torch.Generator(device).manual_seed(seed)
+    return _randn((n_rows, n_cols), g, device, scale, dtype)
+
+
+def random_gelu_inputs(n: int, seed: int, dtype: str = "fp32", scale: float = 1.0,
+                       device: str | torch.device = "cpu"):
+    """Seeded x, w, b of n elements for the fused GELU: N(0, scale^2) draws in
+    that order from one generator on ``device``, cast to ``dtype``."""
+    g = torch.Generator(device).manual_seed(seed)
+    return tuple(_randn((n,), g, device, scale, dtype) for _ in range(3))
