@@ -1,8 +1,18 @@
-"""Summarise rocprofv3 CSV output for the attention kernel into a short markdown file.
+"""Summarise rocprofv3 CSV output into a short markdown file.
 
-    python3 -m tiled_attention_tileattn_amd.rocprof_summary OUT_DIR \
+    python3 -m tiled_attention_tileattn_amd.rocprof_summary \
         --trace DIR --fetch DIR --write DIR --sq DIR --copy-fetch DIR --copy-write DIR \
         --out profiles/NAME.md --commands "cmd1" "cmd2" ...
+
+    python3 -m tiled_attention_tileattn_amd.rocprof_summary --generic SPEC_JSON \
+        --trace DIR --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
+        --title TITLE --out profiles/NAME.md --commands ...
+
+The first form covers the attention kernel (with the SQ counter pass and the
+figures bench.py reads back).  The generic form takes a JSON list of kernels,
+each {"key": "sub1&sub2", "label": ..., "flop": F} or {..., "bytes": B}: the
+key's substrings must all occur in the kernel name, and F / B is the
+algorithmic work of one launch; it prints one table row per kernel.
 
 Each DIR is a ``rocprofv3 -f csv -d DIR -o run`` output directory of one pass
 (kernel trace with --stats; then one --pmc pass per counter group).  The copy
@@ -52,16 +62,75 @@ def counters(d: str, key: str):
 
 def trace_stats(d: str, key: str):
     for r in _csv(d, "kernel_stats.csv"):
-        if key in r["Name"]:
+        if _match(key, r["Name"]):
             return {"calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
                     "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])}
     raise KeyError(key)
 
 
+def _match(key: str, name: str) -> bool:
+    return all(part in name for part in key.split("&"))
+
+
+def counters_matching(d: str, key: str):
+    acc = {}
+    for r in _csv(d, "counter_collection.csv"):
+        if _match(key, r["Kernel_Name"]):
+            acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: statistics.fmean(v) for k, v in acc.items()}
+
+
+def copy_scales(copy_fetch: str, copy_write: str):
+    cf = counters(copy_fetch, "copyBuffer").get("FETCH_SIZE") or \
+        counters(copy_fetch, "elementwise")["FETCH_SIZE"]
+    cw = counters(copy_write, "copyBuffer").get("WRITE_SIZE") or \
+        counters(copy_write, "elementwise")["WRITE_SIZE"]
+    return cf, cw, COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
+
+
+def generic(a):
+    spec = json.loads(a.generic)
+    cf, cw, f_scale, w_scale = copy_scales(a.copy_fetch, a.copy_write)
+    lines = [f"# rocprofv3: {a.title}", "",
+             "Kernel trace (with --stats) and FETCH_SIZE / WRITE_SIZE passes, each a separate run.",
+             f"Counter bytes are scaled by what the counters read for a plain 256 MiB copy "
+             f"(FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}).", "",
+             "| kernel | workload | calls | avg time | algorithmic rate | HBM fetch | HBM write | algorithmic bytes |",
+             "|---|---|---|---|---|---|---|---|"]
+    figs = []
+    for k in spec:
+        tr = trace_stats(a.trace, k["key"])
+        fk = counters_matching(a.fetch, k["key"]).get("FETCH_SIZE", float("nan"))
+        wk = counters_matching(a.write, k["key"]).get("WRITE_SIZE", float("nan"))
+        fb, wb = fk * 1024.0 * f_scale, wk * 1024.0 * w_scale
+        avg = tr["avg_ns"] * 1e-9
+        if "flop" in k:
+            rate = f"{k['flop'] / avg / 1e12:.1f} TFLOP/s"
+            algo = k.get("bytes")
+        else:
+            rate = f"{k['bytes'] / avg / 1e9:.0f} GB/s"
+            algo = k["bytes"]
+        lines.append(f"| `{k['key'].replace('&', ' ')}` | {k['label']} | {tr['calls']} | {tr['avg_ns']/1e3:.1f} us "
+                     f"(min {tr['min_ns']/1e3:.1f}) | {rate} | {fb/2**20:.1f} MiB | {wb/2**20:.1f} MiB | "
+                     f"{'%.1f MiB' % (algo / 2**20) if algo else '-'} |")
+        figs.append({"key": k["key"], "label": k["label"], "calls": tr["calls"], "avg_kernel_ns": tr["avg_ns"],
+                     "fetch_bytes": fb, "write_bytes": wb, **{x: k[x] for x in ("flop", "bytes") if x in k}})
+    lines += ["", f"Copy calibration (256 MiB copy): FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB.", "",
+              "Commands (run from the repository root, `export TMPDIR=/tmp`):", ""]
+    lines += [f"    {c}" for c in a.commands] + ["", "```json", json.dumps(figs, indent=1), "```", ""]
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
-    for k in ("trace", "fetch", "write", "sq", "copy-fetch", "copy-write"):
+    for k in ("trace", "fetch", "write", "copy-fetch", "copy-write"):
         ap.add_argument(f"--{k}", required=True)
+    ap.add_argument("--sq")
+    ap.add_argument("--generic", default=None, help="JSON list of kernels (generic form)")
+    ap.add_argument("--title", default="")
     ap.add_argument("--out", required=True)
     ap.add_argument("--workload", default="causal_gqa_bf16 (B=1, Hq=32, Hkv=8, S=8192, D=128)")
     ap.add_argument("--flop", type=float, default=549755813888.0)
@@ -70,6 +139,11 @@ def main():
     ap.add_argument("--bench-log", default=None,
                     help="stdout of the profiled bench.py run (its JSON line)")
     a = ap.parse_args()
+    if a.generic:
+        generic(a)
+        return
+    if not a.sq:
+        ap.error("--sq is required for the attention summary")
 
     tr = trace_stats(a.trace, KERNEL_KEY)
     fetch_kib = counters(a.fetch, KERNEL_KEY)["FETCH_SIZE"]
