@@ -37,7 +37,8 @@
 //     vector phase (the online softmax), half a tile apart, so that one wave
 //     keeps the matrix core busy while the other exponentiates.
 //   * exp is computed as exp2 with scale*log2(e) folded into one FMA; the
-//     reference max is raised lazily (see softmax_tile), which is exact.
+//     reference max is raised lazily, only when a tile's exponentials grow
+//     too large (see softmax_tile), which is exact.
 //   * Causal: tiles entirely above a workgroup's diagonal are never loaded;
 //     masking code runs only on tiles that cross a wave's diagonal or the
 //     ragged end.  A wave whose rows end before the workgroup's last tile
@@ -49,6 +50,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <float.h>
 #include <math.h>
 #include <type_traits>
 
@@ -72,6 +74,7 @@ constexpr int kF32Threads = kF32Waves * 64;
 constexpr int kF32BlockM = kF32Waves * kRowsPerWave;   // fp32 path: 128 query rows
 constexpr int kBlockNF32 = 32;                         // keys per tile (fp32 path)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format,
 // no swizzle, no stride): loads past num_records return 0.
 constexpr int kBufferFlags = 0x00020000;
@@ -136,8 +139,10 @@ __device__ __forceinline__ void map_workgroup(int hw_id, int nwg, int Hkv, int G
 #ifndef TILEATTN_BF16_WAVES
 #define TILEATTN_BF16_WAVES 8
 #endif
-#ifndef TILEATTN_RESCALE_THRESHOLD
-#define TILEATTN_RESCALE_THRESHOLD 8.0f
+// Largest sum of one lane's p of a tile before the reference max is raised
+// (2^8: every p stays <= 2^8).
+#ifndef TILEATTN_RESCALE_SUM
+#define TILEATTN_RESCALE_SUM 256.0f
 #endif
 #ifndef TILEATTN_SETPRIO
 #define TILEATTN_SETPRIO 1
@@ -169,52 +174,59 @@ struct Bf16Tile {
 };
 
 // Steps (2)-(4a) of the tile update for one lane's 32 scores of its query row.
-// The reference max m_run is raised only when some row's tile max exceeds it
-// by more than TILEATTN_RESCALE_THRESHOLD (log2 units; a wave-uniform branch),
-// which leaves the result exact: numerator and denominator are accumulated
-// against the same m_run, and p <= 2^threshold stays far from fp32/bf16
-// overflow.  When the branch is taken every lane rescales its accumulator and
-// running sum by alpha = exp2((m_old - m_new) * c).  The running sum adds the
-// fp32 p; p is then packed to bf16 (round to nearest even) in the B-operand
-// layout of the P*V product.  Masked scores are -inf; with c > 0 they give
-// p = exp2(-inf) = 0.
-template <bool IS_F16, bool GUARD, int NACC>
-__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& m_run, float& l_run,
+// mref is the row's reference maximum in exp2 units (m * c).  The tile is
+// first exponentiated against the current reference, p = exp2(s c - mref).
+// Only if some lane's sum of those p exceeds TILEATTN_RESCALE_SUM (a
+// wave-uniform ballot; rare after a row's first tile) is the reference
+// raised to the row's tile maximum, the accumulator and running sum scaled
+// by alpha = exp2(mref_old - mref_new), and the tile exponentiated again.
+// Numerator and denominator are always accumulated against the same
+// reference, so the result is exact, and every p stays at most
+// TILEATTN_RESCALE_SUM, far from fp32/bf16/fp16 overflow.  The reference
+// starts at -FLT_MAX (finite): against it a visible score gives p = inf,
+// which takes the raising branch, and a masked (-inf) score gives 0, so no
+// step forms inf - inf.  The running sum adds the fp32 p; p is packed to
+// 16 bits (round to nearest even) in the B-operand layout of the P*V
+// product.
+template <bool IS_F16, int NACC>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& mref, float& l_run,
                                              float c, f32x16 (&acc)[NACC],
                                              bf16x8 (&pf)[2][2]) {
-  float mx = fmaxf(s[0][0], s[0][1]);
+  auto exponentiate = [&](float m) -> float {
+    float psum0, psum1;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
-  mx = wave_pair_max(mx);
-  const bool grow = (m_run == -INFINITY) || ((mx - m_run) * c > TILEATTN_RESCALE_THRESHOLD);
-  if (__builtin_expect(__ballot(grow) != 0, 0)) {  // rare after the first tile
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
-    m_run = m_new;
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * t + e], c, -m));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * t + e + 1], c, -m));
+          const bool first = kb == 0 && t == 0 && e == 0;
+          psum0 = first ? p0 : psum0 + p0;
+          psum1 = first ? p1 : psum1 + p1;
+          pf[kb][t][e] = round16<IS_F16>(p0);
+          pf[kb][t][e + 1] = round16<IS_F16>(p1);
+        }
+    return psum0 + psum1;
+  };
+  float ps = exponentiate(mref);
+  if (__builtin_expect(__ballot(!(ps <= TILEATTN_RESCALE_SUM)) != 0, 0)) {
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+    mx = wave_pair_max(mx);
+    const float m_new = fmaxf(mref, mx * c);  // c > 0
+    const float alpha = __builtin_amdgcn_exp2f(mref - m_new);
+    mref = m_new;
     l_run *= alpha;
 #pragma unroll
     for (int i = 0; i < NACC; ++i) acc[i] *= alpha;
+    ps = exponentiate(mref);
   }
-  // GUARD: a row that has seen no visible key yet keeps m_run = -inf; its
-  // masked scores must still give p = 0, not exp2(-inf + inf).
-  const float mc = (GUARD && m_run == -INFINITY) ? 0.f : m_run * c;
-  float psum0 = 0.f, psum1 = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * t + e], c, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * t + e + 1], c, -mc));
-        psum0 += p0;
-        psum1 += p1;
-        pf[kb][t][e] = round16<IS_F16>(p0);
-        pf[kb][t][e + 1] = round16<IS_F16>(p1);
-      }
-  l_run += psum0 + psum1;
+  l_run += ps;
 }
 
 // Ping-pong schedule.  The 8 waves form two groups (waves 0-3 and 4-7, one
@@ -370,7 +382,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
   f32x16 s[2] = {f32x16{}, f32x16{}};
   bf16x8 pf[2][2];
-  float m_run = -INFINITY;
+  float mref = -FLT_MAX;  // reference max in exp2 units (see softmax_tile)
   float l_run = 0.f;
   // exp2 argument scale, scale*log2(e), kept >= the smallest normal float: a
   // zero (or tiny) scale then still gives every visible key p = exp2(~0) = 1
@@ -463,7 +475,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
       }
       // c > 0 here, so a masked (-inf) score gives p = exp2(-inf) = 0 without
       // a separate masked code path.
-      softmax_tile<IS_F16, MASK>(s, m_run, l_run, c, acc, pf);
+      softmax_tile<IS_F16>(s, mref, l_run, c, acc, pf);
     }
     if constexpr (ALIBI)
       if (j + 1 < nt) bias_init(j + 1);
@@ -528,10 +540,10 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     }
   }
 
-  // ---- epilogue: O = acc / l, lse = m*scale + ln l --------------------------
+  // ---- epilogue: O = acc / l, lse = m*scale + ln l = mref*ln2 + ln l ---------
   const float l_tot = wave_pair_sum(l_run);
-  // Block mask: a row with no visible key (l = 0, m = -inf) gets o = 0,
-  // lse = -inf.
+  // Block mask: a row with no visible key (l = 0, mref = -FLT_MAX) gets
+  // o = 0, lse = -inf.
   const float inv = (MASK && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
   if (my_row < Sq) {
     uint16_t* orow = O + (q_head + my_row) * D;
@@ -549,7 +561,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
               ((uint32_t)__builtin_bit_cast(uint16_t, o4[3]) << 16);
         *reinterpret_cast<uint2*>(orow + db * 32 + 8 * g + 4 * half) = u;
       }
-    if (half == 0) LSE[q_head + my_row] = m_run * kscale + logf(l_tot);
+    if (half == 0) LSE[q_head + my_row] = mref * kLn2 + logf(l_tot);
   }
 }
 
