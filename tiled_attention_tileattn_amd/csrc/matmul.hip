@@ -53,7 +53,10 @@ constexpr int kLoads = kBM * kBK / 8 / kThreads;  // 16-byte loads per thread pe
 static_assert(kLoads == 4 && kBK * kBN / 8 / kThreads == 4, "tile / thread count mismatch");
 constexpr unsigned kOutOfRange = 0x80000000u;  // beyond any buffer range used here
 constexpr int kBufferFlags = 0x00020000;
-constexpr int kGroupM = 8;                      // tile rows per group of the tile order
+#ifndef TILEATTN_MM_GROUP
+#define TILEATTN_MM_GROUP 4
+#endif
+constexpr int kGroupM = TILEATTN_MM_GROUP;      // tile rows per group of the tile order
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
