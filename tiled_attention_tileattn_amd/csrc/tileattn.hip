@@ -113,22 +113,40 @@ __device__ __forceinline__ __bf16 round16(float x) {
 }
 
 // Map a hardware workgroup id to (batch, query head, query tile).  Ids are
-// dealt to the 8 XCDs round-robin; the remap gives each XCD a contiguous range
-// of the logical order (batch, kv head, query tile [heaviest first if causal],
-// query head within the group), so an XCD's resident workgroups share K/V.
+// dealt to the 8 XCDs round-robin (XCD = id % 8, position on it = id / 8).
+// The remap gives every XCD whole (batch, kv head) slots, so its resident
+// workgroups share K/V in its L2, and orders each XCD's share by query tile,
+// heaviest first when causal, across all of its slots (longest jobs first on
+// its 32 CUs), then by query head within the group.  With fewer than 8 slots
+// a slot's query tiles are spread over 8/slots XCDs by residue, so every XCD
+// gets the same mix of heavy and light tiles.  Shapes that divide unevenly
+// keep contiguous XCD ranges of the order (batch, kv head, query tile, query
+// head), or the plain order.
 __device__ __forceinline__ void map_workgroup(int hw_id, int nwg, int Hkv, int G, int nqt,
                                               bool causal, int& b, int& hq, int& qt) {
-  int logical = hw_id;
-  if ((nwg & 7) == 0) {
-    const int per_xcd = nwg >> 3;
-    logical = (hw_id & 7) * per_xcd + (hw_id >> 3);
+  const int P = nwg / (G * nqt);  // (batch, kv head) slots
+  const int x = hw_id & 7, pos = hw_id >> 3;
+  int slot, tq, g;
+  if ((P & 7) == 0) {
+    const int per = P >> 3;
+    g = pos % G;
+    const int rest = pos / G;
+    slot = x * per + rest % per;
+    tq = rest / per;
+  } else if (P < 8 && 8 % P == 0 && nqt % (8 / P) == 0) {
+    const int r = 8 / P;
+    g = pos % G;
+    slot = x / r;
+    tq = x % r + (pos / G) * r;
+  } else {
+    const int logical = (nwg & 7) == 0 ? x * (nwg >> 3) + pos : hw_id;
+    g = logical % G;
+    const int rest = logical / G;
+    tq = rest % nqt;
+    slot = rest / nqt;
   }
-  const int g = logical % G;
-  int rest = logical / G;
-  const int tq = rest % nqt;
-  rest /= nqt;
-  const int hk = rest % Hkv;
-  b = rest / Hkv;
+  const int hk = slot % Hkv;
+  b = slot / Hkv;
   hq = hk * G + g;
   qt = causal ? (nqt - 1 - tq) : tq;
 }
