@@ -163,6 +163,26 @@ def test_causal_row_zero_is_first_value_row():
     assert torch.equal(o.cpu()[:, :, 0], v.repeat_interleave(2, dim=1)[:, :, 0])
 
 
+# Shapes that exercise each branch of the workgroup -> (batch, head, tile) map:
+# whole (batch, kv head) slots per XCD (slots a multiple of 8), slots spread
+# over XCDs by query-tile residue (1, 2 or 4 slots), and the uneven fallback.
+MAP_CASES = [
+    # B, Hq, Hkv, S, D, causal
+    (1, 8, 1, 2048, 128, True),     # 1 slot, 8 query tiles: residue split over 8 XCDs
+    (2, 4, 2, 1024, 128, True),     # 4 slots, 4 query tiles: residue split over 2 XCDs
+    (1, 4, 2, 2048, 64, False),     # 2 slots, 8 query tiles: residue split over 4 XCDs
+    (8, 2, 2, 512, 64, True),       # 16 slots: 2 whole slots per XCD
+    (1, 8, 2, 1030, 64, True),      # 2 slots, 5 query tiles: uneven, fallback order
+    (3, 4, 1, 600, 64, False),      # 3 slots: fallback order
+]
+
+
+@pytest.mark.parametrize("case", MAP_CASES)
+def test_workgroup_map_cases(case):
+    B, Hq, Hkv, S, D, causal = case
+    _parity(B, Hq, Hkv, S, S, D, causal, "bf16", seed=B * 100 + Hq + S)
+
+
 def test_gqa_equals_mha_with_repeated_kv_bitwise():
     q, k, v = random_qkv(1, 8, 2, 300, 300, 128, dtype="bf16", seed=15)
     o1, l1 = _gpu_forward(q, k, v, True, 0.0883883461356163)

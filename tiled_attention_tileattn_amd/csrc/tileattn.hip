@@ -206,7 +206,12 @@ struct Bf16Tile {
 // step forms inf - inf.  The running sum adds the fp32 p; p is packed to
 // 16 bits (round to nearest even) in the B-operand layout of the P*V
 // product.
-template <bool IS_F16, int NACC>
+//
+// MAX_FIRST takes the tile max before exponentiating instead (a v_max3 tree
+// on every tile, the reference raised when the max exceeds it by more than
+// 8 in log2 units): for score layouts whose max keeps rising from tile to
+// tile, as with a two-sided linear bias, it avoids exponentiating twice.
+template <bool IS_F16, bool MAX_FIRST, int NACC>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& mref, float& l_run,
                                              float c, f32x16 (&acc)[NACC],
                                              bf16x8 (&pf)[2][2]) {
@@ -228,21 +233,32 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& mref, float&
         }
     return psum0 + psum1;
   };
-  float ps = exponentiate(mref);
-  if (__builtin_expect(__ballot(!(ps <= TILEATTN_RESCALE_SUM)) != 0, 0)) {
+  auto raise_to_tile_max = [&]() {
     float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
-    mx = wave_pair_max(mx);
-    const float m_new = fmaxf(mref, mx * c);  // c > 0
+    return wave_pair_max(mx) * c;  // c > 0
+  };
+  auto rescale = [&](float m_new) {
     const float alpha = __builtin_amdgcn_exp2f(mref - m_new);
     mref = m_new;
     l_run *= alpha;
 #pragma unroll
     for (int i = 0; i < NACC; ++i) acc[i] *= alpha;
+  };
+  float ps;
+  if constexpr (MAX_FIRST) {
+    const float mxc = raise_to_tile_max();
+    if (__builtin_expect(__ballot(mxc - mref > 8.0f) != 0, 0)) rescale(fmaxf(mref, mxc));
     ps = exponentiate(mref);
+  } else {
+    ps = exponentiate(mref);
+    if (__builtin_expect(__ballot(!(ps <= TILEATTN_RESCALE_SUM)) != 0, 0)) {
+      rescale(fmaxf(mref, raise_to_tile_max()));
+      ps = exponentiate(mref);
+    }
   }
   l_run += ps;
 }
@@ -324,9 +340,14 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     __syncthreads();
     nt = tcount;
   }
-  auto tile = [&](int j) -> int { return MASK ? (int)(tlist[j] & 0xFFF) : j; };
+  // With a causal linear bias the largest scores of a row sit next to its
+  // diagonal: walking the tiles from the diagonal down finds the row max on
+  // the first visible tile, so the lazy reference is rarely raised after it.
+  constexpr bool kReversed = ALIBI && CAUSAL;
+  auto order = [&](int j) -> int { return kReversed ? nt - 1 - j : j; };
+  auto tile = [&](int j) -> int { return MASK ? (int)(tlist[order(j)] & 0xFFF) : order(j); };
   // This wave's 64-row query block may see tile j (block mask).
-  auto wave_sees = [&](int j) -> bool { return !MASK || ((tlist[j] >> (12 + (wave >> 1))) & 1); };
+  auto wave_sees = [&](int j) -> bool { return !MASK || ((tlist[order(j)] >> (12 + (wave >> 1))) & 1); };
 
   // With the bias, scores are kept in units of 1/kscale: the S product
   // starts from bias/kscale instead of 0 (see bias_init), so the softmax and
@@ -493,7 +514,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
       }
       // c > 0 here, so a masked (-inf) score gives p = exp2(-inf) = 0 without
       // a separate masked code path.
-      softmax_tile<IS_F16>(s, mref, l_run, c, acc, pf);
+      softmax_tile<IS_F16, ALIBI && !CAUSAL>(s, mref, l_run, c, acc, pf);
     }
     if constexpr (ALIBI)
       if (j + 1 < nt) bias_init(j + 1);
