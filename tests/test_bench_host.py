@@ -45,3 +45,13 @@ def test_window_mask_shape():
     for qb in range(16):
         seen = set(np.nonzero(m[qb])[0])
         assert seen == {0} | set(range(max(0, qb - 2), qb + 1))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    import subprocess
+
+    root = Path(__file__).resolve().parents[1]
+    r = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
