@@ -45,8 +45,13 @@
 //     runs the remaining tiles fully masked (p = 0), which keeps both wave
 //     groups in step with the shared barriers.
 //   * Workgroup ids are remapped so the workgroups that one XCD (8 per chip,
-//     ids dealt round-robin) runs share a key/value head and read its K/V
-//     tiles from that XCD's L2; causal query tiles go heaviest first.
+//     ids dealt round-robin) runs share key/value heads and read their K/V
+//     tiles from that XCD's L2, and each XCD takes its causal query tiles
+//     heaviest first across all of its heads (see map_workgroup).
+//   * Instances with a block mask compact the visible key tiles into an LDS
+//     list and skip, per wave, the tiles its rows cannot see; instances with
+//     a linear (ALiBi) bias start the score product from the bias, and walk
+//     the key tiles from the diagonal down when causal.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
