@@ -89,13 +89,14 @@ def tileattn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream) 
 
 def tileattn_fwd_f16(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream) -> int:
     return load_library().tileattn_fwd_f16(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D,
-                                           scale, causal, stream)
+                                           float(scale), int(bool(causal)), stream)
 
 
 def tileattn_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, alibi_slopes,
                      block_mask, mask_heads, is_f16, stream) -> int:
-    return load_library().tileattn_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal,
-                                           alibi_slopes, block_mask, mask_heads, is_f16, stream)
+    return load_library().tileattn_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, float(scale),
+                                           int(bool(causal)), alibi_slopes, block_mask, mask_heads,
+                                           int(bool(is_f16)), stream)
 
 
 def tileattn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream) -> int:
