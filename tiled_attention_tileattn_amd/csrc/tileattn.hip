@@ -194,6 +194,11 @@ struct Bf16Tile {
   static constexpr int kVBytes = kBlockN * kVPitch;
   static constexpr int kLoads = kBlockN * kChunks / kThreads;  // 16-byte loads per tensor
   static_assert(kLoads >= 1 && kLoads * kThreads == kBlockN * kChunks, "tile/threads mismatch");
+  // Per-wave staging area for Q on the way in and O on the way out: the
+  // wave's 32 rows at the K pitch, so the operand-layout reads of Q are
+  // conflict-free like those of K.
+  static constexpr int kStageBytes = kRowsPerWave * kKPitch;
+  static constexpr int kRowLoads = kRowsPerWave * kChunks / 64;  // 16-byte chunks per lane
 };
 
 // Steps (2)-(4a) of the tile update for one lane's 32 scores of its query row.
@@ -285,7 +290,8 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     const float* __restrict__ slopes, const unsigned char* __restrict__ bmask, int mask_heads) {
   using T = Bf16Tile<D>;
   static_assert(T::kWaves == 8, "two groups of four waves");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::kKBytes + 2 * T::kVBytes];
+  __shared__ __attribute__((aligned(16)))
+  unsigned char smem[2 * T::kKBytes + 2 * T::kVBytes + T::kWaves * T::kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -363,17 +369,22 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
   const float kscale = !ALIBI ? scale : (q_dropped ? 1.f : scale);
   const float sigma = ALIBI ? slopes[hq] / kscale : 0.f;
 
-  bf16x8 qf[D / 16];
+  // The wave's 32 query rows are contiguous in memory.  They are loaded
+  // whole-row (64 lanes x 16 bytes = 1 KiB per instruction; rows past Sq,
+  // or every row when Q drops out, lie outside the buffer range and read as
+  // 0), staged in the wave's LDS area, and read back in the B-operand layout
+  // after the prologue barrier.  O leaves the same way in the epilogue.
+  unsigned char* const stage = smem + 2 * T::kKBytes + 2 * T::kVBytes + wave * T::kStageBytes;
+  u32x4 qreg[T::kRowLoads];
   {
-    const bool ok = my_row < Sq && !q_dropped;
-    const uint16_t* qrow = Q + (q_head + (size_t)(ok ? my_row : 0)) * D;
+    const int rows_here = q_dropped ? 0 : max(0, min(kRowsPerWave, Sq - qw));
+    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Q + (q_head + (size_t)(rows_here > 0 ? qw : 0)) * D), 0, rows_here * D * 2, kBufferFlags);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      uint4 u = ok ? *reinterpret_cast<const uint4*>(qrow + kk * 16 + half * 8)
-                   : make_uint4(0, 0, 0, 0);
-      qf[kk] = __builtin_bit_cast(bf16x8, u);
-    }
+    for (int i = 0; i < T::kRowLoads; ++i)
+      qreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, (i * 64 + lane) * 16, 0, 0));
   }
+  bf16x8 qf[D / 16];
 
   // ---- tile loaders: global -> registers -> LDS ---------------------------
   // Buffer loads over this head's K and V: the tile offset is a scalar, the
@@ -564,12 +575,20 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
   if (!MASK || nt > 0) {
     if constexpr (ALIBI) bias_init(0);
     load_rows(krsrc, tile(0), kreg);
+#pragma unroll
+    for (int i = 0; i < T::kRowLoads; ++i) {
+      const int idx = i * 64 + lane;
+      *reinterpret_cast<u32x4*>(stage + (idx / T::kChunks) * T::kKPitch + (idx % T::kChunks) * 16) = qreg[i];
+    }
     store_rows(kslot(0), T::kKPitch, kreg);
     if (group == 1) {
       if (nt > 1) load_rows(krsrc, tile(1), kreg);
       load_rows(vrsrc, tile(0), vreg);
     }
     __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[kk] = *reinterpret_cast<const bf16x8*>(stage + l32 * T::kKPitch + kk * 32 + half * 16);
 
     if (group == 0) {
       iteration0(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
@@ -589,24 +608,34 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
   // Block mask: a row with no visible key (l = 0, mref = -FLT_MAX) gets
   // o = 0, lse = -inf.
   const float inv = (MASK && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
-  if (my_row < Sq) {
-    uint16_t* orow = O + (q_head + my_row) * D;
+  // The lane's pieces of its row (4 x 4 consecutive d) go to the wave's LDS
+  // area, and the rows leave it whole: 1 KiB per store instruction.
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        __bf16 o4[4];
+    for (int g = 0; g < 4; ++g) {
+      __bf16 o4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = round16<IS_F16>(acc[db][4 * g + e] * inv);
-        uint2 u;
-        u.x = (uint32_t)__builtin_bit_cast(uint16_t, o4[0]) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, o4[1]) << 16);
-        u.y = (uint32_t)__builtin_bit_cast(uint16_t, o4[2]) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, o4[3]) << 16);
-        *reinterpret_cast<uint2*>(orow + db * 32 + 8 * g + 4 * half) = u;
-      }
-    if (half == 0) LSE[q_head + my_row] = mref * kLn2 + logf(l_tot);
+      for (int e = 0; e < 4; ++e) o4[e] = round16<IS_F16>(acc[db][4 * g + e] * inv);
+      uint2 u;
+      u.x = (uint32_t)__builtin_bit_cast(uint16_t, o4[0]) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, o4[1]) << 16);
+      u.y = (uint32_t)__builtin_bit_cast(uint16_t, o4[2]) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, o4[3]) << 16);
+      *reinterpret_cast<uint2*>(stage + l32 * T::kKPitch + (db * 32 + 8 * g + 4 * half) * 2) = u;
+    }
+  __syncthreads();
+  {
+    uint16_t* const oblock = O + (q_head + (size_t)qw) * D;
+#pragma unroll
+    for (int i = 0; i < T::kRowLoads; ++i) {
+      const int idx = i * 64 + lane, r = idx / T::kChunks, cc = idx % T::kChunks;
+      if (qw + r < Sq)
+        *reinterpret_cast<u32x4*>(oblock + r * D + cc * 8) =
+            *reinterpret_cast<const u32x4*>(stage + r * T::kKPitch + cc * 16);
+    }
   }
+  if (half == 0 && my_row < Sq) LSE[q_head + my_row] = mref * kLn2 + logf(l_tot);
 }
 
 // ---------------------------------------------------------------------------
