@@ -86,6 +86,18 @@ constexpr int kBufferFlags = 0x00020000;
 // Capacity of the per-workgroup tile list of block-masked calls: Sk <= 64 * this.
 constexpr int kMaxMaskedTiles = 2048;
 
+// Raw buffer resource over [base, base + bytes) for a wave-uniform range,
+// built from readfirstlane'd values so it lives in scalar registers (a
+// resource the compiler cannot prove uniform costs a loop around every
+// buffer access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_buffer(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(lo | (hi << 32)), 0,
+                                           __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
+}
+
 __device__ __forceinline__ float wave_pair_max(float x) {
   // Lanes l and l^32 hold the same query row; combine their partial maxima.
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -378,8 +390,7 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
   u32x4 qreg[T::kRowLoads];
   {
     const int rows_here = q_dropped ? 0 : max(0, min(kRowsPerWave, Sq - qw));
-    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(Q + (q_head + (size_t)(rows_here > 0 ? qw : 0)) * D), 0, rows_here * D * 2, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t qrsrc = wave_buffer(Q + (q_head + (size_t)(rows_here > 0 ? qw : 0)) * D, rows_here * D * 2);
 #pragma unroll
     for (int i = 0; i < T::kRowLoads; ++i)
       qreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, (i * 64 + lane) * 16, 0, 0));
@@ -626,14 +637,20 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     }
   __syncthreads();
   {
-    uint16_t* const oblock = O + (q_head + (size_t)qw) * D;
+    // All reads first, then the stores: a buffer store past the wave's last
+    // row (Sq) falls outside the buffer range and is dropped, so no store
+    // needs a branch (which would serialise each read with its store).
+    const int rows_here = max(0, min(kRowsPerWave, Sq - qw));
+    const __amdgpu_buffer_rsrc_t orsrc = wave_buffer(O + (q_head + (size_t)(rows_here > 0 ? qw : 0)) * D, rows_here * D * 2);
+    u32x4 orow[T::kRowLoads];
 #pragma unroll
     for (int i = 0; i < T::kRowLoads; ++i) {
-      const int idx = i * 64 + lane, r = idx / T::kChunks, cc = idx % T::kChunks;
-      if (qw + r < Sq)
-        *reinterpret_cast<u32x4*>(oblock + r * D + cc * 8) =
-            *reinterpret_cast<const u32x4*>(stage + r * T::kKPitch + cc * 16);
+      const int idx = i * 64 + lane;
+      orow[i] = *reinterpret_cast<const u32x4*>(stage + (idx / T::kChunks) * T::kKPitch + (idx % T::kChunks) * 16);
     }
+#pragma unroll
+    for (int i = 0; i < T::kRowLoads; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(orow[i], orsrc, (i * 64 + lane) * 16, 0, 0);
   }
   if (half == 0 && my_row < Sq) LSE[q_head + my_row] = mref * kLn2 + logf(l_tot);
 }
