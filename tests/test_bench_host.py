@@ -55,3 +55,16 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        text=True, timeout=300, cwd=root)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_profile_hash_ignores_comments_but_not_code(tmp_path):
+    # bench.py reports the profiled traffic only while the kernel source hash
+    # matches: comment and whitespace edits keep it, a code change does not.
+    from tiled_attention_tileattn_amd.rocprof_summary import SRC, source_hash
+    src = open(SRC).read()
+    a = tmp_path / "a.hip"
+    a.write_text("// a new leading comment\n" + src.replace("\n", "\n  /* note */ \n", 3))
+    b = tmp_path / "b.hip"
+    b.write_text(src.replace("kRowsPerWave = 32", "kRowsPerWave = 16", 1))
+    assert source_hash(str(a)) == source_hash(SRC)
+    assert source_hash(str(b)) != source_hash(SRC)

@@ -29,6 +29,8 @@
 //     operand is read from row-major LDS with ds_read_b64_tr_b16, whose
 //     transpose yields exactly the key order that P^T carries.
 //   * Q lives in VGPRs for the whole loop (B operand of the first product).
+//     It arrives, and O leaves, whole rows at a time through a per-wave LDS
+//     area, since in the MFMA layouts a lane holds only pieces of a row.
 //   * K and V tiles are double-buffered in LDS with padded row pitches (no
 //     bank conflicts); operands are read into a small register ring a few
 //     MFMAs ahead of use.

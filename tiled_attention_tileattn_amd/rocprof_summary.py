@@ -31,6 +31,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 
 KERNEL_KEY = "attn_fwd_16_kernel<128, true, false, false, false>"
@@ -39,8 +40,14 @@ SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "tileattn
 
 
 def source_hash(path: str = SRC) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source with comments and whitespace removed: the
+    recorded figures stay valid across comment edits and go stale with any
+    change to the code itself."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256("".join(text.split()).encode()).hexdigest()[:16]
 
 
 def _csv(d: str, suffix: str):
