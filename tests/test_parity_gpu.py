@@ -268,3 +268,12 @@ def test_workload_sampled_rows(name):
         G = w.Hq // w.Hkv
         v0 = v[:, :, 0].to("cuda").repeat_interleave(G, dim=1)
         assert torch.equal(o[:, :, 0], v0)
+
+
+def test_forward_refuses_outputs_that_overlap_inputs():
+    q, k, v = (t.cuda() for t in random_qkv(1, 2, 1, 64, 64, 64, dtype="bf16", seed=18))
+    with pytest.raises(ValueError, match="must not overlap"):
+        ta.forward(q, k, v, out=q)
+    lse_in_k = k.view(torch.float32).reshape(-1)[: 2 * 64].view(1, 2, 64)
+    with pytest.raises(ValueError, match="must not overlap"):
+        ta.forward(q, k, v, lse=lse_in_k)

@@ -129,6 +129,13 @@ def tileattn_launch_shape(dtype_bytes, B, Hq, Hkv, Sq, Sk, D, causal):
 
 
 # ---- torch convenience wrapper ----------------------------------------------
+def _overlap(a, b) -> bool:
+    """The byte ranges of two contiguous tensors intersect."""
+    a0, b0 = a.data_ptr(), b.data_ptr()
+    a1, b1 = a0 + a.numel() * a.element_size(), b0 + b.numel() * b.element_size()
+    return a0 < b1 and b0 < a1 and a1 > a0 and b1 > b0
+
+
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
             stream=None, alibi_slopes=None, block_mask=None):
     """Attention forward on the GPU: returns (o, lse).
@@ -172,6 +179,9 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     if tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous() \
             or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 tensor [B, Hq, Sq] on q's device")
+    for name, t in (("out", out), ("lse", lse)):
+        if any(_overlap(t, u) for u in (q, k, v)):
+            raise ValueError(f"{name} must not overlap q, k or v")
     ext = alibi_slopes is not None or block_mask is not None
     if ext:
         if q.dtype not in (torch.bfloat16, torch.float16):
