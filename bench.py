@@ -159,6 +159,26 @@ def matmul_lines(ta, steps, warmup):
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 
 
+def device_peak_line(props) -> str:
+    """The dense bf16 MFMA peak recomputed from this device: compute units x
+    4096 FLOP/clk x its peak engine clock (hipDeviceAttributeClockRate, kHz,
+    read through the HIP runtime that torch and the library already use).
+    Printed beside the published figure the metric divides by."""
+    import ctypes
+    cus = props.multi_processor_count
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD)
+        khz = ctypes.c_int(0)
+        # 5 = hipDeviceAttributeClockRate in hip_runtime_api.h's enum
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, torch.cuda.current_device()) != 0 or khz.value <= 0:
+            raise OSError("hipDeviceGetAttribute failed")
+        peak = cus * 4096 * khz.value * 1e3 / 1e12
+        return (f"CUs={cus}, peak engine clock {khz.value / 1e3:.0f} MHz -> dense bf16 peak "
+                f"{peak:.1f} TFLOP/s (the metric uses the published {PEAK_BF16_TFLOPS})")
+    except (OSError, RuntimeError) as e:
+        return f"CUs={cus}, peak engine clock unavailable ({e}); the metric uses the published {PEAK_BF16_TFLOPS}"
+
+
 def rowwise_lines(ta, steps, warmup):
     """Time the row softmax and the fused GELU: algorithmic bytes (inputs read
     once, output written once) per launch over the launch time, in GB/s."""
@@ -274,7 +294,7 @@ def main():
         return
     ta.load_library()
     props = torch.cuda.get_device_properties(0)
-    log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+    log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} {device_peak_line(props)}")
 
     if args.only == "matmul":
         matmul_lines(ta, args.steps, args.warmup)

@@ -136,6 +136,7 @@ def main():
     for k in ("trace", "fetch", "write", "copy-fetch", "copy-write"):
         ap.add_argument(f"--{k}", required=True)
     ap.add_argument("--sq")
+    ap.add_argument("--l2", default=None, help="pass with TCC_HIT_sum and TCC_MISS_sum (L2 hit rate)")
     ap.add_argument("--generic", default=None, help="JSON list of kernels (generic form)")
     ap.add_argument("--title", default="")
     ap.add_argument("--out", required=True)
@@ -175,6 +176,9 @@ def main():
     simds = 1024
     mfma_util = sq.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (gui / xcds * simds)
     lds_conf = sq.get("SQ_LDS_BANK_CONFLICT", float("nan")) / max(sq.get("SQ_LDS_IDX_ACTIVE", 1.0), 1.0)
+    l2 = counters(a.l2, KERNEL_KEY) if a.l2 else {}
+    l2_hits, l2_misses = l2.get("TCC_HIT_sum"), l2.get("TCC_MISS_sum")
+    l2_rate = l2_hits / (l2_hits + l2_misses) if l2_hits is not None and l2_misses is not None else None
     fig = {
         "kernel": KERNEL_KEY,
         "workload": a.workload,
@@ -194,6 +198,7 @@ def main():
         "valu_insts": sq.get("SQ_INSTS_VALU"),
         "mfma_insts": sq.get("SQ_INSTS_MFMA"),
         "lds_insts": sq.get("SQ_INSTS_LDS"),
+        "l2_hit_rate": l2_rate,
         "bench_event_mean_ns": (a.flop / (bench["roofline"]["achieved"] * 1e12) * 1e9) if bench else None,
     }
     lines = [
@@ -216,6 +221,8 @@ def main():
         f"| LDS bank conflicts per active LDS cycle | {lds_conf:.4f} |",
         f"| effective engine clock (GRBM_GUI_ACTIVE/8 / kernel time) | {fig['effective_clock_ghz']:.2f} GHz |",
         f"| VALU / MFMA / LDS instructions | {fig['valu_insts']:.3g} / {fig['mfma_insts']:.3g} / {fig['lds_insts']:.3g} |",
+        (f"| L2 hit rate (TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum); {l2_hits:.3g} hits, {l2_misses:.3g} misses) "
+         f"| {l2_rate*100:.1f} % |") if l2_rate is not None else "| L2 hit rate | not collected |",
         f"| copy calibration (256 MiB copy): FETCH_SIZE / WRITE_SIZE | {cf:.0f} KiB / {cw:.0f} KiB |",
         "",
         "Commands (run from the repository root, `export TMPDIR=/tmp`):",
