@@ -214,28 +214,40 @@ def rowwise_lines(ta, steps, warmup):
     del src, dst
 
 
-def cpu_baseline(w):
-    """Time the fp64 oracle on the whole workload on this host's cores.
+def cpu_baseline(w, sample_rows=None):
+    """Time the fp64 oracle on workload w on this host's cores.
 
     The oracle forms every head's full Sq x Sk score block (causal entries
     masked, not skipped), so it does twice the counted FLOP of a causal
-    workload; the rate reported is the counted FLOP over its time.
+    workload; the rate reported is the counted FLOP over its time.  With
+    ``sample_rows`` it times that many seeded random query rows (each costs
+    the same Sk-key row of work) and extrapolates linearly to every row, and
+    the sample string says so.
     """
     import oracle
     from tiled_attention_tileattn_amd.inputs import make_inputs
 
     q, k, v = make_inputs(w)
     cores = len(os.sched_getaffinity(0))
+    n_rows = w.B * w.Hq * w.Sq
     t0 = time.perf_counter()
-    oracle.attention(q, k, v, w.scale, w.causal, threads=cores)
-    t = time.perf_counter() - t0
+    if sample_rows is None:
+        oracle.attention(q, k, v, w.scale, w.causal, threads=cores)
+        t = t_all = time.perf_counter() - t0
+        sample = f"the whole workload ({n_rows} query rows)"
+    else:
+        rows = np.random.default_rng(w.seed + 7).choice(n_rows, sample_rows, replace=False)
+        oracle.attention_rows(q, k, v, w.scale, w.causal, rows, threads=cores)
+        t = time.perf_counter() - t0
+        t_all = t * n_rows / sample_rows
+        sample = (f"{sample_rows} random query rows of {n_rows}, extrapolated linearly to all rows "
+                  f"({t_all:.0f} s)")
     return {
-        "value": w.flop() / t / 1e12,
+        "value": w.flop() / t_all / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"the whole workload ({w.B * w.Hq * w.Sq} query rows), fp64 numpy oracle with "
-                  f"one BLAS thread per worker thread, {t:.1f} s",
+        "sample": f"{sample}, fp64 numpy oracle with one BLAS thread per worker thread, {t:.1f} s",
     }
 
 
@@ -314,6 +326,9 @@ def main():
             wall, mean, med, mn = time_workload(ta, w, st, wu)
             log(f"{name}: median {med*1e3:.1f} us min {mn*1e3:.1f} us "
                 f"-> {w.flop()/med/1e9:.1f} TFLOP/s ({w.flop()/med/1e9/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
+            if not args.no_cpu:
+                cb = cpu_baseline(w, sample_rows=256 if name == "longctx_gqa_bf16" else None)
+                log(f"{name}: CPU oracle {cb['value']:.3g} TFLOP/s on {cb['cores']} cores ({cb['sample']})")
 
         # ALiBi bias + block masks on the headline shape; work counted over
         # the visible query-key pairs only.
