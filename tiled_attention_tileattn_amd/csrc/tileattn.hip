@@ -184,6 +184,17 @@ __device__ __forceinline__ void map_workgroup(int hw_id, int nwg, int Hkv, int G
 #ifndef TILEATTN_SETPRIO
 #define TILEATTN_SETPRIO 1
 #endif
+// Race-check build: with TILEATTN_SYNC_CHECK defined, extra workgroup
+// barriers close the staging step and both phases of every iteration, in the
+// same number on both wave groups.  Only the order of LDS accesses across
+// waves changes, not the arithmetic, so that build's results must equal the
+// normal build's bit for bit; a difference would expose an LDS read that
+// races the write it depends on.
+#ifdef TILEATTN_SYNC_CHECK
+#define TILEATTN_CHECK_BARRIER() __syncthreads()
+#else
+#define TILEATTN_CHECK_BARRIER() ((void)0)
+#endif
 // Depth (in MFMAs) of the LDS operand prefetch ring of each product.
 #ifndef TILEATTN_PREFETCH
 #define TILEATTN_PREFETCH 4
@@ -565,9 +576,12 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     const bool ld_k = j + 1 < nt, ld_v = j < nt;
     if (ld_k) load_rows(krsrc, tile(j + 1), kreg);
     if (ld_v) load_rows(vrsrc, tile(j), vreg);
+    TILEATTN_CHECK_BARRIER();
     first();
+    TILEATTN_CHECK_BARRIER();
     __builtin_amdgcn_s_barrier();
     second();
+    TILEATTN_CHECK_BARRIER();
     if (ld_k) store_rows(kslot(j + 1), T::kKPitch, kreg);
     if (ld_v) store_rows(vslot(j), T::kVPitch, vreg);
     __syncthreads();
@@ -577,9 +591,12 @@ __global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
     if (j < nt) store_rows(vslot(j), T::kVPitch, vreg);
     if (j + 2 < nt) load_rows(krsrc, tile(j + 2), kreg);
     if (j + 1 < nt) load_rows(vrsrc, tile(j + 1), vreg);
+    TILEATTN_CHECK_BARRIER();
     first();
+    TILEATTN_CHECK_BARRIER();
     __builtin_amdgcn_s_barrier();
     second();
+    TILEATTN_CHECK_BARRIER();
     __syncthreads();
   };
 
