@@ -277,3 +277,10 @@ def test_forward_refuses_outputs_that_overlap_inputs():
     lse_in_k = k.view(torch.float32).reshape(-1)[: 2 * 64].view(1, 2, 64)
     with pytest.raises(ValueError, match="must not overlap"):
         ta.forward(q, k, v, lse=lse_in_k)
+
+
+def test_million_keys_few_queries():
+    # 2^20 + 37 keys: 16385 key tiles per workgroup, the 32-bit buffer
+    # offsets of K and V up to 256 MiB, and a ragged last tile; 3 query rows
+    # keep the oracle cheap.
+    _parity(1, 2, 1, 3, (1 << 20) + 37, 128, False, "bf16", seed=19)
