@@ -179,8 +179,53 @@ MAP_CASES = [
 
 @pytest.mark.parametrize("case", MAP_CASES)
 def test_workgroup_map_cases(case):
+    # These grids are small enough for 128-row workgroups (4 waves); the map
+    # is the same function for both workgroup sizes.
     B, Hq, Hkv, S, D, causal = case
     _parity(B, Hq, Hkv, S, S, D, causal, "bf16", seed=B * 100 + Hq + S)
+
+
+# Grids of more than half a chip of 256-row workgroups keep the 8-wave
+# ping-pong kernel: many heads over short, ragged sequences.
+EIGHT_WAVE_CASES = [
+    # B, Hq, Hkv, Sq, Sk, D, dtype
+    (2, 64, 8, 300, 300, 128, "bf16"),
+    (4, 40, 8, 129, 257, 64, "bf16"),
+    (3, 64, 16, 200, 333, 128, "fp16"),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", EIGHT_WAVE_CASES)
+def test_eight_wave_grids(case, causal):
+    B, Hq, Hkv, Sq, Sk, D, dtype = case
+    st, bm, _, _ = ta.tileattn_launch_shape(2, B, Hq, Hkv, Sq, Sk, D, int(causal))
+    assert st == 0 and bm == 256
+    _parity(B, Hq, Hkv, Sq, Sk, D, causal, dtype, seed=B + Hq + Sq + Sk)
+
+
+def test_small_grids_take_128_row_workgroups():
+    # The workload and sweep shapes on either side of the switch.
+    assert ta.tileattn_launch_shape(2, 4, 8, 8, 1024, 1024, 64, 0)[1] == 128   # mha_bf16
+    assert ta.tileattn_launch_shape(2, 1, 32, 8, 8192, 8192, 128, 1)[1] == 256  # causal GQA 8K
+    assert ta.tileattn_launch_shape(2, 1, 4, 2, 300, 300, 128, 1)[1] == 128
+
+
+def test_eight_wave_residue_map_on_sampled_rows():
+    # One (batch, kv head) slot and 24 query tiles of 256 rows: the 8-wave
+    # kernel's residue split over the XCDs (192 workgroups).
+    B, Hq, Hkv, S, D = 1, 8, 1, 6144, 128
+    assert ta.tileattn_launch_shape(2, B, Hq, Hkv, S, S, D, 1)[1] == 256
+    q, k, v = random_qkv(B, Hq, Hkv, S, S, D, dtype="bf16", seed=20)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    o, lse = _gpu_forward(q, k, v, True, scale)
+    rng = np.random.default_rng(20)
+    rows = np.unique(np.concatenate([rng.integers(0, B * Hq * S, 384),
+                                     [h * S + i for h in range(Hq) for i in (0, 255, 256, S - 1)]]))
+    o_rows = o.reshape(-1, D)[torch.as_tensor(rows, device="cuda")]
+    l_rows = lse.reshape(-1)[torch.as_tensor(rows, device="cuda")]
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, scale, True, rows)
+    _check(o_rows, l_rows, o_ref, lse_ref, "bf16", f"residue map, 8 waves ({len(rows)} rows)")
 
 
 def test_gqa_equals_mha_with_repeated_kv_bitwise():

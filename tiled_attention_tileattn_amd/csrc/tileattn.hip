@@ -59,6 +59,7 @@
 #include <stdint.h>
 #include <float.h>
 #include <math.h>
+#include <atomic>
 #include <type_traits>
 
 #include "../../include/tileattn.h"
@@ -173,9 +174,6 @@ __device__ __forceinline__ void map_workgroup(int hw_id, int nwg, int Hkv, int G
 // ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
-#ifndef TILEATTN_BF16_WAVES
-#define TILEATTN_BF16_WAVES 8
-#endif
 // Largest sum of one lane's p of a tile before the reference max is raised
 // (2^8: every p stays <= 2^8).
 #ifndef TILEATTN_RESCALE_SUM
@@ -200,9 +198,12 @@ __device__ __forceinline__ void map_workgroup(int hw_id, int nwg, int Hkv, int G
 #define TILEATTN_PREFETCH 4
 #endif
 
-template <int D>
+// WAVES = 8: the ping-pong workgroup (256 query rows).  WAVES = 4: 128 query
+// rows, one wave per SIMD, every wave in group 0 (no ping-pong), for grids
+// too small to fill the chip with 256-row workgroups.
+template <int D, int WAVES = 8>
 struct Bf16Tile {
-  static constexpr int kWaves = TILEATTN_BF16_WAVES;
+  static constexpr int kWaves = WAVES;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kBlockM = kWaves * kRowsPerWave;  // query rows per workgroup
   static constexpr int kChunks = D / 8;                    // 16-byte chunks per K/V row
@@ -306,15 +307,17 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& mref, float&
 // M(j).  A barrier separates the halves, so on every SIMD one wave drives the
 // matrix core while the other works through its exponentials.
 // MASK: a block mask (tile list, per-wave skipping, rows with no visible key);
-// ALIBI: the linear bias.  The plain kernel has neither.
-template <int D, bool CAUSAL, bool IS_F16, bool MASK, bool ALIBI>
-__global__ __launch_bounds__(Bf16Tile<D>::kThreads) void attn_fwd_16_kernel(
+// ALIBI: the linear bias.  The plain kernel has neither.  WAVES = 4 runs the
+// same code with group 0 only: each wave does M(j) then V(j), and the group
+// stages every row of each tile (the schedule group 0 follows anyway).
+template <int D, bool CAUSAL, bool IS_F16, bool MASK, bool ALIBI, int WAVES = 8>
+__global__ __launch_bounds__(WAVES * 64) void attn_fwd_16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* K,
     const uint16_t* V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Hq, int Hkv, int Sq, int Sk, float scale, int nqt, int nwg,
     const float* __restrict__ slopes, const unsigned char* __restrict__ bmask, int mask_heads) {
-  using T = Bf16Tile<D>;
-  static_assert(T::kWaves == 8, "two groups of four waves");
+  using T = Bf16Tile<D, WAVES>;
+  static_assert(WAVES == 8 || WAVES == 4, "two groups of four waves, or group 0 alone");
   __shared__ __attribute__((aligned(16)))
   unsigned char smem[2 * T::kKBytes + 2 * T::kVBytes + T::kWaves * T::kStageBytes];
 
@@ -872,19 +875,53 @@ int launch16(Kern kernel, const uint16_t* q, const uint16_t* k, const uint16_t* 
   return e == hipSuccess ? TILEATTN_OK : TILEATTN_ERR_LAUNCH;
 }
 
+// Compute units of the current device, queried once per device.
+int compute_units() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> count[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = count[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    count[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Workgroup size of the plain 16-bit entry points: 256-row workgroups of 8
+// waves unless that grid would leave at least half the compute units idle;
+// then 128-row workgroups of 4 waves, twice as many.
+int waves16(int B, int Hq, int Sq) {
+  const long long wg256 = (long long)B * Hq * ((Sq + 255) / 256);
+  return 2 * wg256 <= compute_units() ? 4 : 8;
+}
+
+template <int D, bool IS_F16, bool MASK, bool ALIBI, int WAVES>
+int launch_waves(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                 int B, int Hq, int Hkv, int Sq, int Sk, float scale, int causal,
+                 const float* slopes, const unsigned char* bmask, int mask_heads, void* stream) {
+  using T = Bf16Tile<D, WAVES>;
+  return causal ? launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, true, IS_F16, MASK, ALIBI, WAVES>,
+                                                    q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, slopes, bmask,
+                                                    mask_heads, stream)
+                : launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, false, IS_F16, MASK, ALIBI, WAVES>,
+                                                    q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, slopes, bmask,
+                                                    mask_heads, stream);
+}
+
 // bf16 and fp16 inputs share one kernel template (IS_F16); a block mask and
-// the linear bias select the MASK / ALIBI instances.
+// the linear bias select the MASK / ALIBI instances (always 8 waves).
 template <int D, bool IS_F16, bool MASK, bool ALIBI>
 int launch_variant(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
                    int B, int Hq, int Hkv, int Sq, int Sk, float scale, int causal,
                    const float* slopes, const unsigned char* bmask, int mask_heads, void* stream) {
-  using T = Bf16Tile<D>;
-  return causal ? launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, true, IS_F16, MASK, ALIBI>, q, k,
-                                                    v, o, lse, B, Hq, Hkv, Sq, Sk, scale, slopes, bmask,
-                                                    mask_heads, stream)
-                : launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, false, IS_F16, MASK, ALIBI>, q, k,
-                                                    v, o, lse, B, Hq, Hkv, Sq, Sk, scale, slopes, bmask,
-                                                    mask_heads, stream);
+  if constexpr (!MASK && !ALIBI)
+    if (waves16(B, Hq, Sq) == 4)
+      return launch_waves<D, IS_F16, MASK, ALIBI, 4>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, causal,
+                                                     slopes, bmask, mask_heads, stream);
+  return launch_waves<D, IS_F16, MASK, ALIBI, 8>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, causal,
+                                                 slopes, bmask, mask_heads, stream);
 }
 
 template <bool IS_F16>
@@ -975,7 +1012,9 @@ extern "C" int tileattn_launch_shape(int dtype_bytes, int B, int Hq, int Hkv, in
   static const float dummy[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
   const int st = validate(dummy, dummy, dummy, dummy, dummy, B, Hq, Hkv, Sq, Sk, D, 1.0f, &empty);
   if (st != TILEATTN_OK) return st;
-  const int bm = dtype_bytes == 2 ? (D == 128 ? Bf16Tile<128>::kBlockM : Bf16Tile<64>::kBlockM)
+  // 16-bit: the plain entry points' choice (the ext entry point always
+  // uses 256-row workgroups).
+  const int bm = dtype_bytes == 2 ? (waves16(B, Hq, Sq) == 4 ? Bf16Tile<128, 4>::kBlockM : Bf16Tile<128, 8>::kBlockM)
                                   : kF32BlockM;
   if (block_m) *block_m = bm;
   if (block_n) *block_n = dtype_bytes == 2 ? kBlockN : kBlockNF32;
