@@ -34,7 +34,7 @@ import os
 import re
 import statistics
 
-KERNEL_KEY = "attn_fwd_16_kernel<128, true, false, false, false>"
+KERNEL_KEY = "attn_fwd_16_kernel<128, true, false, false, false, 8>"
 COPY_BYTES = 256 * 1024 * 1024
 SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "tileattn.hip")
 
