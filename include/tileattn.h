@@ -202,8 +202,12 @@ const char* tileattn_strerror(int status);
 /*
  * Launch geometry the library uses for a problem: query rows per workgroup
  * (block_m), keys per tile (block_n) and the number of workgroups.  For
- * reporting and tests; pure host arithmetic, no HIP call.  dtype_bytes is 2
- * (bf16 or fp16) or 4 (fp32).  Returns TILEATTN_OK or the error tileattn_fwd would.
+ * reporting and tests; host arithmetic plus, for 16-bit inputs, the current
+ * device's compute-unit count (queried once per device; 256 when no device
+ * answers).  dtype_bytes is 2 (bf16 or fp16: the plain entry points, which
+ * use 256-row workgroups, or 128-row ones when the 256-row grid would fill
+ * at most half of the compute units; tileattn_fwd_ext always uses 256) or 4
+ * (fp32).  Returns TILEATTN_OK or the error tileattn_fwd would.
  */
 int tileattn_launch_shape(int dtype_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D,
                           int causal, int* block_m, int* block_n, long long* workgroups);
