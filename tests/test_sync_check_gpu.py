@@ -55,14 +55,19 @@ CASES = [
     (1, 4, 2, 640, 640, 128, True, False, True, False),
     (1, 2, 2, 520, 520, 128, False, True, True, True),
     (1, 4, 2, 2048, 2048, 128, True, False, False, True),
+    # Grids over half a chip of 256-row workgroups: the 8-wave ping-pong
+    # kernel (the small plain shapes above run 128-row workgroups).
+    (2, 64, 8, 300, 300, 128, True, False, False, False),
+    (3, 64, 16, 520, 400, 64, False, False, False, True),
 ]
 
 
 @pytest.mark.parametrize("case", CASES)
 def test_barrier_build_is_bit_identical(libs, case):
     B, Hq, Hkv, Sq, Sk, D, causal, alibi, masked, f16 = case
+    bm = 256 if (alibi or masked) else ta.tileattn_launch_shape(2, B, Hq, Hkv, Sq, Sk, D, int(causal))[1]
     _say(f"sync check B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} D={D} causal={causal} "
-         f"alibi={alibi} mask={masked} fp16={f16}")
+         f"alibi={alibi} mask={masked} fp16={f16} rows/workgroup={bm}")
     q, k, v = (t.cuda() for t in random_qkv(B, Hq, Hkv, Sq, Sk, D, dtype="fp16" if f16 else "bf16",
                                            seed=Sq + Sk + D))
     slopes = alibi_slopes(Hq).cuda() if alibi else None
