@@ -329,3 +329,23 @@ def test_million_keys_few_queries():
     # offsets of K and V up to 256 MiB, and a ragged last tile; 3 query rows
     # keep the oracle cheap.
     _parity(1, 2, 1, 3, (1 << 20) + 37, 128, False, "bf16", seed=19)
+
+
+# Grids on either side of the workgroup-size switch (at most 128 workgroups
+# of 256 rows on a 256-CU device take 128-row workgroups instead).
+SWITCH_CASES = [
+    # B, Hq, Hkv, Sq, Sk, D, causal, dtype
+    (1, 64, 8, 512, 300, 128, True, "bf16"),    # 128 -> 128-row workgroups
+    (1, 43, 43, 700, 700, 64, False, "bf16"),   # 129 -> 256-row
+    (2, 32, 16, 260, 512, 128, False, "fp16"),  # 128 -> 128-row
+    (5, 13, 13, 500, 257, 64, True, "fp16"),    # 130 -> 256-row
+]
+
+
+@pytest.mark.parametrize("case", SWITCH_CASES)
+def test_workgroup_size_switch(case):
+    B, Hq, Hkv, Sq, Sk, D, causal, dtype = case
+    wg256 = B * Hq * -(-Sq // 256)
+    expect = 128 if 2 * wg256 <= torch.cuda.get_device_properties(0).multi_processor_count else 256
+    assert ta.tileattn_launch_shape(2, B, Hq, Hkv, Sq, Sk, D, int(causal))[1] == expect
+    _parity(B, Hq, Hkv, Sq, Sk, D, causal, dtype, seed=wg256 + Sq)
