@@ -225,6 +225,17 @@ struct Bf16Tile {
   // conflict-free like those of K.
   static constexpr int kStageBytes = kRowsPerWave * kKPitch;
   static constexpr int kRowLoads = kRowsPerWave * kChunks / 64;  // 16-byte chunks per lane
+  // LDS layout: K slots 0 and 1, V slots 0 and 1, then the staging areas.
+  // The 4-wave kernel lays its staging areas over the two V slots instead
+  // (Q is staged before the first V tile is written, O after the last one is
+  // read), which keeps its workgroup within 80 KiB of LDS.  Two such
+  // workgroups fit on a CU, so the compiler can hold the kernel to two waves
+  // per SIMD (256 registers per lane): the products then take the VGPR form
+  // of the MFMA, where the one-wave budget moves accumulators through AGPRs.
+  static constexpr bool kStageOverV = WAVES == 4;
+  static constexpr int kStageOff = 2 * kKBytes + (kStageOverV ? 0 : 2 * kVBytes);
+  static constexpr int kSmemBytes = 2 * kKBytes + 2 * kVBytes + (kStageOverV ? 0 : kWaves * kStageBytes);
+  static_assert(!kStageOverV || kWaves * kStageBytes <= 2 * kVBytes, "staging areas must fit in the V slots");
 };
 
 // Steps (2)-(4a) of the tile update for one lane's 32 scores of its query row.
@@ -311,7 +322,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& mref, float&
 // same code with group 0 only: each wave does M(j) then V(j), and the group
 // stages every row of each tile (the schedule group 0 follows anyway).
 template <int D, bool CAUSAL, bool IS_F16, bool MASK, bool ALIBI, int WAVES = 8>
-__global__ __launch_bounds__(WAVES * 64) void attn_fwd_16_kernel(
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* K,
     const uint16_t* V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Hq, int Hkv, int Sq, int Sk, float scale, int nqt, int nwg,
@@ -319,7 +330,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_16_kernel(
   using T = Bf16Tile<D, WAVES>;
   static_assert(WAVES == 8 || WAVES == 4, "two groups of four waves, or group 0 alone");
   __shared__ __attribute__((aligned(16)))
-  unsigned char smem[2 * T::kKBytes + 2 * T::kVBytes + T::kWaves * T::kStageBytes];
+  unsigned char smem[T::kSmemBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -402,7 +413,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_16_kernel(
   // or every row when Q drops out, lie outside the buffer range and read as
   // 0), staged in the wave's LDS area, and read back in the B-operand layout
   // after the prologue barrier.  O leaves the same way in the epilogue.
-  unsigned char* const stage = smem + 2 * T::kKBytes + 2 * T::kVBytes + wave * T::kStageBytes;
+  unsigned char* const stage = smem + T::kStageOff + wave * T::kStageBytes;
   u32x4 qreg[T::kRowLoads];
   {
     const int rows_here = q_dropped ? 0 : max(0, min(kRowsPerWave, Sq - qw));
@@ -622,6 +633,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_16_kernel(
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
       qf[kk] = *reinterpret_cast<const bf16x8*>(stage + l32 * T::kKPitch + kk * 32 + half * 16);
+    // Staging over the V slots: every wave's Q reads complete before any
+    // wave writes V_0 there.
+    if constexpr (T::kStageOverV) __syncthreads();
 
     if (group == 0) {
       iteration0(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
