@@ -18,8 +18,9 @@
 //     group, so the epilogue writes 16-byte (fp32) or 8-byte (bf16) pieces;
 //   * K steps of 64: the next A and B tiles are loaded with buffer loads into
 //     registers at the top of a step, the current tiles are multiplied out
-//     of LDS, and the registers are written to the other LDS slot at the end
-//     (double buffering, one barrier per step);
+//     of LDS, and the registers are written to the other LDS slot between
+//     the MFMA blocks of the step's middle sub-steps (double buffering, one
+//     barrier per step);
 //   * A operand fragments are 16-byte LDS reads along K; B fragments are read
 //     down the columns of the row-major B tile with ds_read_b64_tr_b16;
 //   * padded LDS rows (A: 144 B, B: 576 B) make every operand read phase
@@ -128,11 +129,17 @@ __global__ __launch_bounds__(kThreads) void matmul_bf16_kernel(const uint16_t* A
       breg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[i], 0, 0));
     }
   };
-  auto store_tiles = [&](int stage) {
+  auto store_a = [&](int stage) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int idx = tid + i * kThreads;
       *reinterpret_cast<u32x4*>(smem + stage + (idx >> 3) * kAPitch + (idx & 7) * 16) = areg[i];
+    }
+  };
+  auto store_b = [&](int stage) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int idx = tid + i * kThreads;
       *reinterpret_cast<u32x4*>(smem + stage + kABytes + (idx >> 5) * kBPitch + (idx & 31) * 16) = breg[i];
     }
   };
@@ -165,7 +172,8 @@ __global__ __launch_bounds__(kThreads) void matmul_bf16_kernel(const uint16_t* A
 
   if (nk > 0) {
     load_tiles(0);
-    store_tiles(0);
+    store_a(0);
+    store_b(0);
     __syncthreads();
   }
   for (int kt = 0; kt < nk; ++kt) {
@@ -191,8 +199,12 @@ __global__ __launch_bounds__(kThreads) void matmul_bf16_kernel(const uint16_t* A
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma(bfr[cur][nb], af[cur][mb], acc[nb][mb]);
+      // The staged next tile goes to the other slot (last read in the
+      // previous step, before its closing barrier) between the MFMA blocks of
+      // the middle sub-steps, A after the second and B after the third.
+      if (kt + 1 < nk && t == 1) store_a(((kt + 1) & 1) * kStage);
+      if (kt + 1 < nk && t == 2) store_b(((kt + 1) & 1) * kStage);
     }
-    if (kt + 1 < nk) store_tiles(((kt + 1) & 1) * kStage);
     __syncthreads();
   }
 
