@@ -23,9 +23,11 @@ GELU, g = h / (1 + exp2(-2 L z)), h = fma(x, w, b), z = c (h + a h^3):
     constants c and a: <= 8u relative;
   * exp2 of -2 L z: argument error |2 L z| * 10u, which moves the factor
     1/(1 + e) by at most that (relative), plus 2u for exp2 itself;
-  * 1 + e, the division: 2u.
-  relative error <= (12 + 30 |z|) u, plus 2^-8 for bf16 output, plus the
-  oracle's own absolute error where 1 + tanh cancels (1e-15 |h|) and 2^-125.
+  * 1 + e, the division: 2u.  The bf16 kernel multiplies by the hardware
+    reciprocal instead (1 ulp, i.e. 2u, then the product: u): 4u there.
+  relative error <= (12 + 30 |z|) u (bf16: 2u more), plus 2^-8 for bf16
+  output, plus the oracle's own absolute error where 1 + tanh cancels
+  (1e-15 |h|) and 2^-125.
 """
 
 import math
@@ -66,7 +68,7 @@ def _softmax_bound(x64, p_ref, n, bf16_out):
     dist = np.where(np.isfinite(x64), np.abs(x64 - m), 0.0)   # -inf entries: p_ref = 0
     rel = (2 * dist + 6) * U + gamma
     if bf16_out:
-        rel = rel + 2.0 ** -8
+        rel = rel + 2 * U + 2.0 ** -8
     return rel * p_ref + TINY
 
 
@@ -145,7 +147,7 @@ def _gelu_bound(x, w, b, g_ref, bf16_out):
     z = math.sqrt(2 / math.pi) * (h + 0.044715 * h ** 3)
     rel = (12 + 30 * np.abs(z)) * U
     if bf16_out:
-        rel = rel + 2.0 ** -8
+        rel = rel + 2 * U + 2.0 ** -8
     return rel * np.abs(g_ref) + 1e-15 * np.abs(h) + TINY
 
 

@@ -61,6 +61,7 @@ struct F32 {
   static constexpr int kPer16 = 4;    // elements per 16 bytes
   static constexpr int kWideThreads = TILEATTN_SOFTMAX_F32_WIDE;  // threads per row above 4096 columns
   static constexpr int kUnroll = 2;   // 16-byte accesses per array in flight per thread (GELU)
+  static constexpr bool kRcpDiv = false;  // GELU divides correctly rounded (see gelu_tanh)
   __device__ static void widen16(u32x4 u, float (&v)[kPer16]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(u[e]);
@@ -90,6 +91,7 @@ struct BF16 {
   static constexpr int kBytes = 2;
   static constexpr int kPer16 = 8;
   static constexpr int kUnroll = 4;
+  static constexpr bool kRcpDiv = true;
   static constexpr int kWideThreads = TILEATTN_SOFTMAX_BF16_WIDE;
   __device__ static float widen(uint16_t u) { return __uint_as_float((unsigned)u << 16); }
   __device__ static uint16_t narrow(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }  // RNE
@@ -272,10 +274,17 @@ __global__ __launch_bounds__(kThreads) void softmax_rows_online_kernel(const typ
 }
 
 // tanh-approximate GELU of h, as h * sigmoid(2z), z = c (h + 0.044715 h^3).
+// RCP: h times the hardware reciprocal (v_rcp_f32, about 1 ulp) instead of
+// the correctly rounded division, whose fix-up sequence makes the 16-bit
+// kernel issue-bound.  The extra ulp in fp32 is far below the half ulp of
+// the 16-bit rounding that follows; the edge cases are unchanged (1 + e is
+// 1 or more, or +inf, whose reciprocal is 0 as in h / inf).
+template <bool RCP>
 __device__ __forceinline__ float gelu_tanh(float h) {
   constexpr float kC = 0.7978845608028654f;  // sqrt(2/pi)
   const float z = kC * fmaf(0.044715f * h, h * h, h);
-  return h / (1.0f + __builtin_amdgcn_exp2f(-2.0f * kLog2e * z));
+  const float den = 1.0f + __builtin_amdgcn_exp2f(-2.0f * kLog2e * z);
+  return RCP ? h * __builtin_amdgcn_rcpf(den) : h / den;
 }
 
 // One 16-byte piece of every array per access; each thread keeps
@@ -305,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void gelu_kernel(const typename IO::T* x,
       IO::widen16(wv[u], wf);
       IO::widen16(bv[u], bf);
 #pragma unroll
-      for (int e = 0; e < P; ++e) xf[e] = gelu_tanh(fmaf(xf[e], wf[e], bf[e]));
+      for (int e = 0; e < P; ++e) xf[e] = gelu_tanh<IO::kRcpDiv>(fmaf(xf[e], wf[e], bf[e]));
       st_nt(out + (g + u * step) * P, IO::narrow16(xf));
     }
   }
@@ -315,11 +324,11 @@ __global__ __launch_bounds__(kThreads) void gelu_kernel(const typename IO::T* x,
     IO::widen16(ld_nt(w + g * P), wf);
     IO::widen16(ld_nt(b + g * P), bf);
 #pragma unroll
-    for (int e = 0; e < P; ++e) xf[e] = gelu_tanh(fmaf(xf[e], wf[e], bf[e]));
+    for (int e = 0; e < P; ++e) xf[e] = gelu_tanh<IO::kRcpDiv>(fmaf(xf[e], wf[e], bf[e]));
     st_nt(out + g * P, IO::narrow16(xf));
   }
   for (long long i = pieces * P + (long long)blockIdx.x * kThreads + threadIdx.x; i < n; i += step)
-    IO::store1(out + i, gelu_tanh(fmaf(IO::load1(x + i), IO::load1(w + i), IO::load1(b + i))));
+    IO::store1(out + i, gelu_tanh<IO::kRcpDiv>(fmaf(IO::load1(x + i), IO::load1(w + i), IO::load1(b + i))));
 }
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
