@@ -239,12 +239,14 @@ def rowwise_lines(ta, steps, warmup):
     del src, dst
 
 
-def cpu_baseline(w, sample_rows=None):
+def cpu_baseline(w, sample_rows=None, min_seconds=10.0):
     """Time the fp64 oracle on workload w on this host's cores.
 
     The oracle forms every head's full Sq x Sk score block (causal entries
     masked, not skipped), so it does twice the counted FLOP of a causal
-    workload; the rate reported is the counted FLOP over its time.  With
+    workload; the rate reported is the counted FLOP over its time.  A whole
+    workload that takes less than ``min_seconds`` is run again until that
+    much time has passed, and the rate is the mean over the passes.  With
     ``sample_rows`` it times that many seeded random query rows (each costs
     the same Sk-key row of work) and extrapolates linearly to every row, and
     the sample string says so.
@@ -257,9 +259,16 @@ def cpu_baseline(w, sample_rows=None):
     n_rows = w.B * w.Hq * w.Sq
     t0 = time.perf_counter()
     if sample_rows is None:
-        oracle.attention(q, k, v, w.scale, w.causal, threads=cores)
-        t = t_all = time.perf_counter() - t0
-        sample = f"the whole workload ({n_rows} query rows)"
+        passes = 0
+        while True:
+            oracle.attention(q, k, v, w.scale, w.causal, threads=cores)
+            passes += 1
+            t = time.perf_counter() - t0
+            if t >= min_seconds:
+                break
+        t_all = t / passes
+        sample = (f"the whole workload ({n_rows} query rows), {passes} pass{'es' if passes > 1 else ''} "
+                  f"of {t_all * 1e3:.1f} ms" if t_all < 1 else f"of {t_all:.2f} s")
     else:
         rows = np.random.default_rng(w.seed + 7).choice(n_rows, sample_rows, replace=False)
         oracle.attention_rows(q, k, v, w.scale, w.causal, rows, threads=cores)
