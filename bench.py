@@ -267,8 +267,8 @@ def cpu_baseline(w, sample_rows=None, min_seconds=10.0):
             if t >= min_seconds:
                 break
         t_all = t / passes
-        sample = (f"the whole workload ({n_rows} query rows), {passes} pass{'es' if passes > 1 else ''} "
-                  f"of {t_all * 1e3:.1f} ms" if t_all < 1 else f"of {t_all:.2f} s")
+        per_pass = f"{t_all * 1e3:.1f} ms" if t_all < 1 else f"{t_all:.2f} s"
+        sample = f"the whole workload ({n_rows} query rows), {passes} pass{'es' if passes > 1 else ''} of {per_pass}"
     else:
         rows = np.random.default_rng(w.seed + 7).choice(n_rows, sample_rows, replace=False)
         oracle.attention_rows(q, k, v, w.scale, w.causal, rows, threads=cores)

@@ -68,3 +68,13 @@ def test_profile_hash_ignores_comments_but_not_code(tmp_path):
     b.write_text(src.replace("kRowsPerWave = 32", "kRowsPerWave = 16", 1))
     assert source_hash(str(a)) == source_hash(SRC)
     assert source_hash(str(b)) != source_hash(SRC)
+
+
+def test_cpu_baseline_repeats_passes_and_names_them():
+    from tiled_attention_tileattn_amd.inputs import WORKLOADS
+
+    w = WORKLOADS["tiny_fp32"]
+    cb = bench.cpu_baseline(w, min_seconds=0.05)
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+    assert cb["sample"].startswith(f"the whole workload ({w.B * w.Hq * w.Sq} query rows), ")
+    assert " pass" in cb["sample"] and "fp64 numpy oracle" in cb["sample"]
