@@ -239,6 +239,18 @@ def rowwise_lines(ta, steps, warmup):
     del src, dst
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or 'unknown CPU'."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(w, sample_rows=None, min_seconds=10.0):
     """Time the fp64 oracle on workload w on this host's cores.
 
@@ -256,6 +268,7 @@ def cpu_baseline(w, sample_rows=None, min_seconds=10.0):
 
     q, k, v = make_inputs(w)
     cores = len(os.sched_getaffinity(0))
+    cpu = cpu_model()
     n_rows = w.B * w.Hq * w.Sq
     t0 = time.perf_counter()
     if sample_rows is None:
@@ -281,7 +294,7 @@ def cpu_baseline(w, sample_rows=None, min_seconds=10.0):
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"{sample}, fp64 numpy oracle with one BLAS thread per worker thread, {t:.1f} s",
+        "sample": f"{sample}, fp64 numpy oracle with one BLAS thread per worker thread, {t:.1f} s, on {cpu}",
     }
 
 

@@ -45,11 +45,11 @@ routine, brute force); see ``tests/test_oracle_pins.py``,
 ``tests/test_oracle_rowwise_pins.py``.
 """
 
-from .full_softmax import attention, attention_rows, visible_count
+from .full_softmax import attention, attention_rows
 from .biased import attention_ext
 from .brute import attention_bruteforce
 from .matmul import matmul, matmul_rows
 from .rowwise import gelu_fused, softmax_rows
 
-__all__ = ["attention", "attention_rows", "visible_count", "attention_ext", "attention_bruteforce",
+__all__ = ["attention", "attention_rows", "attention_ext", "attention_bruteforce",
            "matmul", "matmul_rows", "softmax_rows", "gelu_fused"]

@@ -56,14 +56,6 @@ def _check_shapes(q, k, v):
     return B, Hq, Hkv, Sq, Sk, D
 
 
-def visible_count(i: np.ndarray, Sk: int, causal: bool) -> np.ndarray:
-    """Number of keys query row i may attend to (causal: keys 0..min(i, Sk-1))."""
-    i = np.asarray(i)
-    if not causal:
-        return np.full(i.shape, Sk, dtype=np.int64)
-    return np.minimum(i + 1, Sk).astype(np.int64)
-
-
 def _head_rows(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: np.ndarray,
                scale: float, causal: bool):
     """Attention of the query rows ``rows`` of one head against one K/V head.

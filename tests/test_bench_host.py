@@ -78,3 +78,4 @@ def test_cpu_baseline_repeats_passes_and_names_them():
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
     assert cb["sample"].startswith(f"the whole workload ({w.B * w.Hq * w.Sq} query rows), ")
     assert " pass" in cb["sample"] and "fp64 numpy oracle" in cb["sample"]
+    assert cb["sample"].endswith(f" on {bench.cpu_model()}")

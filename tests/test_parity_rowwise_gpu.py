@@ -68,7 +68,7 @@ def _softmax_bound(x64, p_ref, n, bf16_out):
     dist = np.where(np.isfinite(x64), np.abs(x64 - m), 0.0)   # -inf entries: p_ref = 0
     rel = (2 * dist + 6) * U + gamma
     if bf16_out:
-        rel = rel + 2 * U + 2.0 ** -8
+        rel = rel + 2.0 ** -8
     return rel * p_ref + TINY
 
 
