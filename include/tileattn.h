@@ -205,8 +205,9 @@ const char* tileattn_strerror(int status);
  * reporting and tests; host arithmetic plus, for 16-bit inputs, the current
  * device's compute-unit count (queried once per device; 256 when no device
  * answers).  dtype_bytes is 2 (bf16 or fp16: the plain entry points, which
- * use 256-row workgroups, or 128-row ones when the 256-row grid would fill
- * at most half of the compute units; tileattn_fwd_ext always uses 256) or 4
+ * use 256-row workgroups, or the key split's 128-row ones when the 256-row
+ * grid would fill at most half of the compute units; tileattn_fwd_ext with
+ * a bias or a block mask always uses 256) or 4
  * (fp32).  Returns TILEATTN_OK or the error tileattn_fwd would.
  */
 int tileattn_launch_shape(int dtype_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D,

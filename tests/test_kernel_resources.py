@@ -2,10 +2,10 @@
 metadata of ``libtileattn.so`` with ``llvm-readelf``, runs nothing).
 
 Every kernel holds its working set in registers, except two families of
-16-bit attention instances with D = 128 that spill a few registers outside
-the tile loop: the linear-bias (ALiBi) instances, whose bias terms add to the
-staged K/V rows, and the 4-wave instances, which stage twice as many K/V
-chunks per thread.  Their per-lane scratch is bounded here so that a change
+16-bit attention instances with D = 128 that spill a few registers: the
+linear-bias (ALiBi) instances, whose bias terms add to the staged K/V rows,
+and the key-split instances, whose groups each stage a whole tile (twice the
+K/V chunks per thread of the 256-row kernel).  Their per-lane scratch is bounded here so that a change
 that spills more (or spills elsewhere) fails on the CPU."""
 
 import os
@@ -23,10 +23,10 @@ READELF = next((p for p in ("/opt/rocm/llvm/bin/llvm-readelf", shutil.which("llv
 BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 
 # (template-argument pattern of the mangled name, max bytes of scratch per lane)
-# attn_fwd_16_kernel<D, CAUSAL, IS_F16, MASK, ALIBI, WAVES>
+# attn_fwd_16_kernel<D, CAUSAL, IS_F16, MASK, ALIBI, SPLIT>
 SPILL_BOUNDS = [
-    (r"attn_fwd_16_kernelILi128ELb[01]ELb[01]ELb[01]ELb1ELi8E", 64),   # D = 128, linear bias
-    (r"attn_fwd_16_kernelILi128ELb[01]ELb[01]ELb0ELb0ELi4E", 80),      # D = 128, 4 waves
+    (r"attn_fwd_16_kernelILi128ELb[01]ELb[01]ELb[01]ELb1ELb0E", 64),   # D = 128, linear bias
+    (r"attn_fwd_16_kernelILi128ELb[01]ELb[01]ELb0ELb0ELb1E", 80),      # D = 128, key split
 ]
 
 

@@ -113,6 +113,25 @@ def test_sweep_fp32(shape, causal):
     _parity(*shape, causal=causal, dtype="fp32", seed=7 + sum(shape))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("heavy_half", [0, 1])
+def test_key_split_merge_with_the_row_max_in_one_half(heavy_half, D):
+    # This grid is small enough for the key split: one wave group takes key
+    # tiles 0-9 (keys 0-639), the other tiles 10-19, the last one past Sk.
+    # Keys of one half scaled by 3 put every row's max in that half, so the
+    # merge scales the other half's partial state down by a large factor.
+    B, Hq, Hkv, Sq, Sk = 1, 4, 2, 200, 1153
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    what = f"key split, max in half {heavy_half}, D={D}"
+    _say(what)
+    q, k, v = random_qkv(B, Hq, Hkv, Sq, Sk, D, dtype="bf16", seed=90 + heavy_half + D)
+    sl = slice(0, 640) if heavy_half == 0 else slice(640, Sk)
+    k[:, :, sl] = (k[:, :, sl].float() * 3).to(k.dtype)
+    o, lse = _gpu_forward(q, k, v, False, scale)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, False)
+    _check(o, lse, o_ref, lse_ref, "bf16", what)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 def test_scale_edge_values(dtype):
     # scale = 0: every visible key weighs the same; large scale: peaky softmax.
@@ -179,8 +198,8 @@ MAP_CASES = [
 
 @pytest.mark.parametrize("case", MAP_CASES)
 def test_workgroup_map_cases(case):
-    # These grids are small enough for 128-row workgroups (4 waves); the map
-    # is the same function for both workgroup sizes.
+    # These grids are small enough for the key split's 128-row workgroups;
+    # the map is the same function for both workgroup sizes.
     B, Hq, Hkv, S, D, causal = case
     _parity(B, Hq, Hkv, S, S, D, causal, "bf16", seed=B * 100 + Hq + S)
 

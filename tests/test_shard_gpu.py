@@ -1,9 +1,13 @@
 """What one GPU can show of a multi-GPU split (needs an MI355X).
 
-* Head sharding: at the causal GQA 8K shape (B=1, Hq=32, Hkv=8, S=8192,
-  D=128) each of 8 GPUs would run the same kernel on one KV head and its 4
-  query heads.  Every such shard, launched on its own, must give bit for bit
-  the rows the full launch gives for those heads.
+* Head sharding: each of 8 GPUs would run the kernel on one KV head and its
+  query heads, with no communication.  At the 32K shape (B=1, Hq=64, Hkv=8)
+  a shard still fills the chip with 256-row workgroups, runs the same kernel
+  instance as the full launch, and must give its rows bit for bit.  At the
+  8K headline shape (B=1, Hq=32, Hkv=8) a shard's grid is small enough for
+  the key split (128-row workgroups, each key range in two halves merged at
+  the end), so it rounds differently; there its rows must agree with the full
+  launch's within the plain path's bf16 tolerances.
 * Key sharding (non-causal): each shard computes (O_g, lse_g) over its keys;
   the exact result is lse = ln sum_g exp(lse_g), O = sum_g exp(lse_g - lse) O_g.
   The merge is done on the host here and compared with the oracle over all
@@ -38,21 +42,33 @@ def _device():
     torch.cuda.synchronize()
 
 
-def test_head_shards_of_causal_gqa_8k_match_the_full_launch():
-    w = WORKLOADS["causal_gqa_bf16"]
-    _say(f"head shards of {w.name}")
+def _head_shards(name):
+    w = WORKLOADS[name]
     q, k, v = make_inputs(w, device="cuda")
-    o, lse = ta.forward(q, k, v, causal=True, scale=w.scale)
+    o, lse = ta.forward(q, k, v, causal=w.causal, scale=w.scale)
     G = w.Hq // w.Hkv
     for g in range(w.Hkv):
         hs = slice(g * G, (g + 1) * G)
-        qs = q[:, hs].contiguous()
-        ks = k[:, g:g + 1].contiguous()
-        vs = v[:, g:g + 1].contiguous()
-        o_s, lse_s = ta.forward(qs, ks, vs, causal=True, scale=w.scale)
+        o_s, lse_s = ta.forward(q[:, hs].contiguous(), k[:, g:g + 1].contiguous(),
+                                v[:, g:g + 1].contiguous(), causal=w.causal, scale=w.scale)
         torch.cuda.synchronize()
-        assert torch.equal(o_s, o[:, hs]), f"shard {g}: O differs"
-        assert torch.equal(lse_s, lse[:, hs]), f"shard {g}: lse differs"
+        yield g, o_s, lse_s, o[:, hs], lse[:, hs]
+
+
+def test_head_shards_of_causal_gqa_32k_match_the_full_launch_bitwise():
+    _say("head shards of longctx_gqa_bf16")
+    for g, o_s, lse_s, o_f, lse_f in _head_shards("longctx_gqa_bf16"):
+        assert torch.equal(o_s, o_f), f"shard {g}: O differs"
+        assert torch.equal(lse_s, lse_f), f"shard {g}: lse differs"
+
+
+def test_head_shards_of_causal_gqa_8k_match_the_full_launch():
+    _say("head shards of causal_gqa_bf16")
+    for g, o_s, lse_s, o_f, lse_f in _head_shards("causal_gqa_bf16"):
+        d = (o_s.float() - o_f.float()).abs()
+        dl = (lse_s - lse_f).abs().max().item()
+        _say(f"  shard {g}: max|dO|={d.max().item():.3e} mean|dO|={d.mean().item():.3e} max|dlse|={dl:.3e}")
+        assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3 and dl <= 1e-4, f"shard {g}"
 
 
 @pytest.mark.parametrize("split", [[700], [64, 1000], [333, 334]])

@@ -50,6 +50,12 @@
 //     ids dealt round-robin) runs share key/value heads and read their K/V
 //     tiles from that XCD's L2, and each XCD takes its causal query tiles
 //     heaviest first across all of its heads (see map_workgroup).
+//   * Grids too small to fill the chip with 256-row workgroups take the key
+//     split instead: 128 query rows per workgroup, which both wave groups
+//     hold, each group running the same ping-pong over its own half of the
+//     key tiles (its own LDS slots, staged one tile ahead); at the end the
+//     two partial (acc, l, max) states of a row merge through LDS by the
+//     online-softmax update itself.
 //   * Instances with a block mask compact the visible key tiles into an LDS
 //     list and skip, per wave, the tiles its rows cannot see; instances with
 //     a linear (ALiBi) bias start the score product from the bias, and walk
@@ -80,14 +86,18 @@ constexpr int kMaxMaskedTiles = 2048;
 #define TILEATTN_PREFETCH 4
 #endif
 
-// WAVES = 8: the ping-pong workgroup (256 query rows).  WAVES = 4: 128 query
-// rows, one wave per SIMD, every wave in group 0 (no ping-pong), for grids
-// too small to fill the chip with 256-row workgroups.
-template <int D, int WAVES = 8>
+// The 8-wave ping-pong workgroup: 256 query rows, every wave with its own 32.
+// SPLIT: 128 query rows, which both wave groups hold, each group visiting
+// half of the key tiles; the two partial results merge at the end.  That is
+// for grids too small to fill the chip with 256-row workgroups.
+template <int D, bool SPLIT = false>
 struct Bf16Tile {
-  static constexpr int kWaves = WAVES;
+  static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kBlockM = kWaves * kRowsPerWave;  // query rows per workgroup
+  static constexpr int kRowWaves = SPLIT ? kWaves / 2 : kWaves;  // waves with distinct query rows
+  static constexpr int kBlockM = kRowWaves * kRowsPerWave;      // query rows per workgroup
+  static constexpr int kStagers = SPLIT ? kThreads / 2 : kThreads;  // threads staging one tile
+  static constexpr int kSets = SPLIT ? 2 : 1;                    // K/V slot pairs (one per group)
   static constexpr int kChunks = D / 8;                    // 16-byte chunks per K/V row
   // LDS row pitches (bytes).  K rows are padded by 16 bytes: the 16 rows of
   // one K-operand read phase (same 16-byte chunk of consecutive keys) then
@@ -100,24 +110,24 @@ struct Bf16Tile {
   static constexpr int kVPitch = D * 2 + 64;
   static constexpr int kKBytes = kBlockN * kKPitch;
   static constexpr int kVBytes = kBlockN * kVPitch;
-  static constexpr int kLoads = kBlockN * kChunks / kThreads;  // 16-byte loads per tensor
-  static_assert(kLoads >= 1 && kLoads * kThreads == kBlockN * kChunks, "tile/threads mismatch");
+  static constexpr int kLoads = kBlockN * kChunks / kStagers;  // 16-byte loads per tensor
+  static_assert(kLoads >= 1 && kLoads * kStagers == kBlockN * kChunks, "tile/threads mismatch");
   // Per-wave staging area for Q on the way in and O on the way out: the
   // wave's 32 rows at the K pitch, so the operand-layout reads of Q are
   // conflict-free like those of K.
   static constexpr int kStageBytes = kRowsPerWave * kKPitch;
   static constexpr int kRowLoads = kRowsPerWave * kChunks / 64;  // 16-byte chunks per lane
-  // LDS layout: K slots 0 and 1, V slots 0 and 1, then the staging areas.
-  // The 4-wave kernel lays its staging areas over the two V slots instead
+  // LDS layout: K slots 0 and 1, V slots 0 and 1, then the staging areas
+  // (one per row wave).  The split kernel has two such slot pairs per tensor
+  // (set g for group g) and lays its staging areas over the V slots instead
   // (Q is staged before the first V tile is written, O after the last one is
-  // read), which keeps its workgroup within 80 KiB of LDS.  Two such
-  // workgroups fit on a CU, so the compiler can hold the kernel to two waves
-  // per SIMD (256 registers per lane): the products then take the VGPR form
-  // of the MFMA, where the one-wave budget moves accumulators through AGPRs.
-  static constexpr bool kStageOverV = WAVES == 4;
-  static constexpr int kStageOff = 2 * kKBytes + (kStageOverV ? 0 : 2 * kVBytes);
-  static constexpr int kSmemBytes = 2 * kKBytes + 2 * kVBytes + (kStageOverV ? 0 : kWaves * kStageBytes);
-  static_assert(!kStageOverV || kWaves * kStageBytes <= 2 * kVBytes, "staging areas must fit in the V slots");
+  // read), which keeps it within 148 KiB at D = 128.
+  static constexpr bool kStageOverV = SPLIT;
+  static constexpr int kVOff = kSets * 2 * kKBytes;
+  static constexpr int kStageOff = kVOff + (kStageOverV ? 0 : kSets * 2 * kVBytes);
+  static constexpr int kSmemBytes = kVOff + kSets * 2 * kVBytes + (kStageOverV ? 0 : kRowWaves * kStageBytes);
+  static_assert(!kStageOverV || kRowWaves * kStageBytes <= kSets * 2 * kVBytes,
+                "staging areas must fit in the V slots");
 };
 
 // Steps (2)-(4a) of the tile update for one lane's 32 scores of its query row.
@@ -200,17 +210,18 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], float& mref, float&
 // M(j).  A barrier separates the halves, so on every SIMD one wave drives the
 // matrix core while the other works through its exponentials.
 // MASK: a block mask (tile list, per-wave skipping, rows with no visible key);
-// ALIBI: the linear bias.  The plain kernel has neither.  WAVES = 4 runs the
-// same code with group 0 only: each wave does M(j) then V(j), and the group
-// stages every row of each tile (the schedule group 0 follows anyway).
-template <int D, bool CAUSAL, bool IS_F16, bool MASK, bool ALIBI, int WAVES = 8>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_16_kernel(
+// ALIBI: the linear bias.  The plain kernel has neither.  SPLIT: the key
+// split of the plain kernel (see Bf16Tile): the same schedule, with group g
+// on its own half of the tiles, staged into its own slots.
+template <int D, bool CAUSAL, bool IS_F16, bool MASK, bool ALIBI, bool SPLIT = false>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* K,
     const uint16_t* V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Hq, int Hkv, int Sq, int Sk, float scale, int nqt, int nwg,
     const float* __restrict__ slopes, const unsigned char* __restrict__ bmask, int mask_heads) {
-  using T = Bf16Tile<D, WAVES>;
-  static_assert(WAVES == 8 || WAVES == 4, "two groups of four waves, or group 0 alone");
+  using T = Bf16Tile<D, SPLIT>;
+  static_assert(T::kThreads == 512, "two groups of four waves");
+  static_assert(!SPLIT || (!MASK && !ALIBI), "the key split serves the plain kernel");
   __shared__ __attribute__((aligned(16)))
   unsigned char smem[T::kSmemBytes];
 
@@ -226,7 +237,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   map_workgroup(blockIdx.x, nwg, Hkv, G, nqt, CAUSAL, b, hq, qt);
   const int hk = hq / G;
   const int q0 = qt * T::kBlockM;
-  const int qw = q0 + wave * kRowsPerWave;
+  const int rw = SPLIT ? (wave & 3) : wave;  // row wave: which 32 rows of the workgroup
+  const int qw = q0 + rw * kRowsPerWave;
   const int my_row = qw + l32;
 
   const size_t q_head = ((size_t)b * Hq + hq) * (size_t)Sq;
@@ -277,7 +289,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   // the first visible tile, so the lazy reference is rarely raised after it.
   constexpr bool kReversed = ALIBI && CAUSAL;
   auto order = [&](int j) -> int { return kReversed ? nt - 1 - j : j; };
-  auto tile = [&](int j) -> int { return MASK ? (int)(tlist[order(j)] & 0xFFF) : order(j); };
+  // Key split: group g visits tiles g*h to g*h + h - 1 of the nkt, with
+  // h = ceil(nkt / 2).  When nkt is odd, group 1's last tile lies past the
+  // keys (past Sk, or past every row's diagonal): its loads read zeros, the
+  // mask hides every score, and it changes nothing.
+  const int tbase = SPLIT ? group * ((nkt + 1) / 2) : 0;
+  if (SPLIT) nt = (nkt + 1) / 2;
+  auto tile = [&](int j) -> int { return MASK ? (int)(tlist[order(j)] & 0xFFF) : tbase + order(j); };
   // This wave's 64-row query block may see tile j (block mask).
   auto wave_sees = [&](int j) -> bool { return !MASK || ((tlist[order(j)] >> (12 + (wave >> 1))) & 1); };
 
@@ -295,9 +313,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   // or every row when Q drops out, lie outside the buffer range and read as
   // 0), staged in the wave's LDS area, and read back in the B-operand layout
   // after the prologue barrier.  O leaves the same way in the epilogue.
-  unsigned char* const stage = smem + T::kStageOff + wave * T::kStageBytes;
+  // Split: the two waves of a row pair share one staging area; group 0
+  // stages Q there and writes O out of it.
+  const bool row_owner = !SPLIT || group == 0;
+  unsigned char* const stage = smem + T::kStageOff + rw * T::kStageBytes;
   u32x4 qreg[T::kRowLoads];
-  {
+  if (row_owner) {
     const int rows_here = q_dropped ? 0 : max(0, min(kRowsPerWave, Sq - qw));
     const __amdgpu_buffer_rsrc_t qrsrc = wave_buffer(Q + (q_head + (size_t)(rows_here > 0 ? qw : 0)) * D, rows_here * D * 2);
 #pragma unroll
@@ -314,11 +335,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, 0, kv_bytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, 0, kv_bytes, kBufferFlags);
   u32x4 kreg[T::kLoads], vreg[T::kLoads];
+  // Split: each group stages its own tiles (thread tid & 255 of the group).
+  const int stid = SPLIT ? (tid & 255) : tid;
   auto load_rows = [&](const __amdgpu_buffer_rsrc_t& rsrc, int j, u32x4 (&reg)[T::kLoads]) {
     const int tile_off = j * kBlockN * D * 2;
 #pragma unroll
     for (int i = 0; i < T::kLoads; ++i) {
-      const int idx = tid + i * T::kThreads;
+      const int idx = stid + i * T::kStagers;
       const int r = idx / T::kChunks, cc = idx % T::kChunks;
       reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (r * D + cc * 8) * 2, tile_off, 0));
     }
@@ -326,13 +349,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   auto store_rows = [&](int byte0, int pitch, const u32x4 (&reg)[T::kLoads]) {
 #pragma unroll
     for (int i = 0; i < T::kLoads; ++i) {
-      const int idx = tid + i * T::kThreads;
+      const int idx = stid + i * T::kStagers;
       const int r = idx / T::kChunks, cc = idx % T::kChunks;
       *reinterpret_cast<u32x4*>(smem + byte0 + r * pitch + cc * 16) = reg[i];
     }
   };
-  auto kslot = [](int j) { return (j & 1) * T::kKBytes; };
-  auto vslot = [](int j) { return 2 * T::kKBytes + (j & 1) * T::kVBytes; };
+  const int set = SPLIT ? group : 0;  // this group's slot pair
+  auto kslot = [&](int j) { return (2 * set + (j & 1)) * T::kKBytes; };
+  auto vslot = [&](int j) { return T::kVOff + (2 * set + (j & 1)) * T::kVBytes; };
 
   const int s16 = lane & 15;
   const int k_lane_off = l32 * T::kKPitch + 16 * half;
@@ -501,13 +525,15 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   if (!MASK || nt > 0) {
     if constexpr (ALIBI) bias_init(0);
     load_rows(krsrc, tile(0), kreg);
+    if (row_owner) {
 #pragma unroll
-    for (int i = 0; i < T::kRowLoads; ++i) {
-      const int idx = i * 64 + lane;
-      *reinterpret_cast<u32x4*>(stage + (idx / T::kChunks) * T::kKPitch + (idx % T::kChunks) * 16) = qreg[i];
+      for (int i = 0; i < T::kRowLoads; ++i) {
+        const int idx = i * 64 + lane;
+        *reinterpret_cast<u32x4*>(stage + (idx / T::kChunks) * T::kKPitch + (idx % T::kChunks) * 16) = qreg[i];
+      }
     }
     store_rows(kslot(0), T::kKPitch, kreg);
-    if (group == 1) {
+    if (SPLIT || group == 1) {
       if (nt > 1) load_rows(krsrc, tile(1), kreg);
       load_rows(vrsrc, tile(0), vreg);
     }
@@ -519,7 +545,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
     // wave writes V_0 there.
     if constexpr (T::kStageOverV) __syncthreads();
 
-    if (group == 0) {
+    if (group == 0 && SPLIT) {
+      // Split: group 0 stages its own tiles one iteration ahead, as group 1
+      // does (no other group writes half of them).
+      iteration1(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
+      for (int j = 1; j < nt; ++j)
+        iteration1(j, [&] { matrix_phase(TT{}, TT{}, j); }, [&] { vector_phase(j); });
+      iteration1(nt, [&] { matrix_phase(FF{}, TT{}, nt); }, [&] {});
+    } else if (group == 0) {
       iteration0(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
       for (int j = 1; j < nt; ++j)
         iteration0(j, [&] { matrix_phase(TT{}, TT{}, j); }, [&] { vector_phase(j); });
@@ -532,29 +565,71 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
     }
   }
 
+  // ---- key split: merge group 1's partial state into group 0's -------------
+  // Each group holds acc, l and the reference max of the same 32 rows over
+  // its half of the keys, both against their own reference.  Group 1's goes
+  // through LDS (over the K slots, free after the loop); group 0 rescales
+  // both to the larger reference and adds: the same update as the online
+  // softmax takes between two tiles.
+  if constexpr (SPLIT) {
+    constexpr int kXchg = 64 * (D / 2 + 2);  // floats per row pair
+    static_assert(T::kRowWaves * kXchg * 4 <= T::kVOff, "exchange must fit in the K slots");
+    float* const xchg = reinterpret_cast<float*>(smem) + rw * kXchg;
+    if (group == 1) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(xchg + ((db * 4 + q4) * 64 + lane) * 4) =
+              f32x4{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]};
+      xchg[64 * (D / 2) + lane] = mref;
+      xchg[64 * (D / 2) + 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (group == 0) {
+      const float m1 = xchg[64 * (D / 2) + lane];
+      const float l1 = xchg[64 * (D / 2) + 64 + lane];
+      const float m = fmaxf(mref, m1);
+      const float a0 = __builtin_amdgcn_exp2f(mref - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(xchg + ((db * 4 + q4) * 64 + lane) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[db][4 * q4 + e] = fmaf(acc[db][4 * q4 + e], a0, x[e] * a1);
+        }
+      l_run = fmaf(l_run, a0, l1 * a1);
+      mref = m;
+    }
+  }
+
   // ---- epilogue: O = acc / l, lse = m*scale + ln l = mref*ln2 + ln l ---------
   const float l_tot = wave_pair_sum(l_run);
   // Block mask: a row with no visible key (l = 0, mref = -FLT_MAX) gets
   // o = 0, lse = -inf.
   const float inv = (MASK && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
   // The lane's pieces of its row (4 x 4 consecutive d) go to the wave's LDS
-  // area, and the rows leave it whole: 1 KiB per store instruction.
+  // area, and the rows leave it whole: 1 KiB per store instruction.  Split:
+  // group 0 alone writes the rows (group 1 only meets the barrier).
+  if (row_owner) {
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      __bf16 o4[4];
+      for (int g = 0; g < 4; ++g) {
+        __bf16 o4[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = round16<IS_F16>(acc[db][4 * g + e] * inv);
-      uint2 u;
-      u.x = (uint32_t)__builtin_bit_cast(uint16_t, o4[0]) |
-            ((uint32_t)__builtin_bit_cast(uint16_t, o4[1]) << 16);
-      u.y = (uint32_t)__builtin_bit_cast(uint16_t, o4[2]) |
-            ((uint32_t)__builtin_bit_cast(uint16_t, o4[3]) << 16);
-      *reinterpret_cast<uint2*>(stage + l32 * T::kKPitch + (db * 32 + 8 * g + 4 * half) * 2) = u;
-    }
+        for (int e = 0; e < 4; ++e) o4[e] = round16<IS_F16>(acc[db][4 * g + e] * inv);
+        uint2 u;
+        u.x = (uint32_t)__builtin_bit_cast(uint16_t, o4[0]) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, o4[1]) << 16);
+        u.y = (uint32_t)__builtin_bit_cast(uint16_t, o4[2]) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, o4[3]) << 16);
+        *reinterpret_cast<uint2*>(stage + l32 * T::kKPitch + (db * 32 + 8 * g + 4 * half) * 2) = u;
+      }
+  }
   __syncthreads();
-  {
+  if (row_owner) {
     // All reads first, then the stores: a buffer store past the wave's last
     // row (Sq) falls outside the buffer range and is dropped, so no store
     // needs a branch (which would serialise each read with its store).
@@ -570,7 +645,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
     for (int i = 0; i < T::kRowLoads; ++i)
       __builtin_amdgcn_raw_buffer_store_b128(orow[i], orsrc, (i * 64 + lane) * 16, 0, 0);
   }
-  if (half == 0 && my_row < Sq) LSE[q_head + my_row] = mref * kLn2 + logf(l_tot);
+  if (row_owner && half == 0 && my_row < Sq) LSE[q_head + my_row] = mref * kLn2 + logf(l_tot);
 }
 
 // ---------------------------------------------------------------------------
@@ -785,39 +860,39 @@ int compute_units() {
   return n;
 }
 
-// Workgroup size of the plain 16-bit entry points: 256-row workgroups of 8
-// waves unless that grid would leave at least half the compute units idle;
-// then 128-row workgroups of 4 waves, twice as many.
-int waves16(int B, int Hq, int Sq) {
+// The plain 16-bit kernel runs 256-row workgroups unless that grid would
+// leave at least half the compute units idle; then the key split's 128-row
+// workgroups, twice as many, each wave with half the tiles.
+bool use_split(int B, int Hq, int Sq) {
   const long long wg256 = (long long)B * Hq * ((Sq + 255) / 256);
-  return 2 * wg256 <= compute_units() ? 4 : 8;
+  return 2 * wg256 <= compute_units();
 }
 
-template <int D, bool IS_F16, bool MASK, bool ALIBI, int WAVES>
+template <int D, bool IS_F16, bool MASK, bool ALIBI, bool SPLIT>
 int launch_waves(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
                  int B, int Hq, int Hkv, int Sq, int Sk, float scale, int causal,
                  const float* slopes, const unsigned char* bmask, int mask_heads, void* stream) {
-  using T = Bf16Tile<D, WAVES>;
-  return causal ? launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, true, IS_F16, MASK, ALIBI, WAVES>,
+  using T = Bf16Tile<D, SPLIT>;
+  return causal ? launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, true, IS_F16, MASK, ALIBI, SPLIT>,
                                                     q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, slopes, bmask,
                                                     mask_heads, stream)
-                : launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, false, IS_F16, MASK, ALIBI, WAVES>,
+                : launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, false, IS_F16, MASK, ALIBI, SPLIT>,
                                                     q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, slopes, bmask,
                                                     mask_heads, stream);
 }
 
 // bf16 and fp16 inputs share one kernel template (IS_F16); a block mask and
-// the linear bias select the MASK / ALIBI instances (always 8 waves).
+// the linear bias select the MASK / ALIBI instances (always 256-row).
 template <int D, bool IS_F16, bool MASK, bool ALIBI>
 int launch_variant(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
                    int B, int Hq, int Hkv, int Sq, int Sk, float scale, int causal,
                    const float* slopes, const unsigned char* bmask, int mask_heads, void* stream) {
   if constexpr (!MASK && !ALIBI)
-    if (waves16(B, Hq, Sq) == 4)
-      return launch_waves<D, IS_F16, MASK, ALIBI, 4>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, causal,
+    if (use_split(B, Hq, Sq))
+      return launch_waves<D, IS_F16, MASK, ALIBI, true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, causal,
+                                                        slopes, bmask, mask_heads, stream);
+  return launch_waves<D, IS_F16, MASK, ALIBI, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, causal,
                                                      slopes, bmask, mask_heads, stream);
-  return launch_waves<D, IS_F16, MASK, ALIBI, 8>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, causal,
-                                                 slopes, bmask, mask_heads, stream);
 }
 
 template <bool IS_F16>
@@ -910,7 +985,7 @@ extern "C" int tileattn_launch_shape(int dtype_bytes, int B, int Hq, int Hkv, in
   if (st != TILEATTN_OK) return st;
   // 16-bit: the plain entry points' choice (the ext entry point always
   // uses 256-row workgroups).
-  const int bm = dtype_bytes == 2 ? (waves16(B, Hq, Sq) == 4 ? Bf16Tile<128, 4>::kBlockM : Bf16Tile<128, 8>::kBlockM)
+  const int bm = dtype_bytes == 2 ? (use_split(B, Hq, Sq) ? Bf16Tile<128, true>::kBlockM : Bf16Tile<128>::kBlockM)
                                   : kF32BlockM;
   if (block_m) *block_m = bm;
   // 16-bit: 64-key tiles.
