@@ -60,14 +60,19 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 def test_profile_hash_ignores_comments_but_not_code(tmp_path):
     # bench.py reports the profiled traffic only while the kernel source hash
     # matches: comment and whitespace edits keep it, a code change does not.
-    from tiled_attention_tileattn_amd.rocprof_summary import SRC, source_hash
-    src = open(SRC).read()
+    from tiled_attention_tileattn_amd.rocprof_summary import KERNEL_SOURCES, SRC, source_hash
+    src, common = KERNEL_SOURCES
+    assert src == SRC and source_hash() == source_hash(src, common)
+    text = open(src).read()
     a = tmp_path / "a.hip"
-    a.write_text("// a new leading comment\n" + src.replace("\n", "\n  /* note */ \n", 3))
+    a.write_text("// a new leading comment\n" + text.replace("\n", "\n  /* note */ \n", 3))
     b = tmp_path / "b.hip"
-    b.write_text(src.replace("kRowsPerWave = 32", "kRowsPerWave = 16", 1))
-    assert source_hash(str(a)) == source_hash(SRC)
-    assert source_hash(str(b)) != source_hash(SRC)
+    b.write_text(text.replace("kRowsPerWave = 32", "kRowsPerWave = 16", 1))
+    c = tmp_path / "c.h"
+    c.write_text(open(common).read().replace("256.0f", "128.0f", 1))
+    assert source_hash(str(a), common) == source_hash()
+    assert source_hash(str(b), common) != source_hash()
+    assert source_hash(src, str(c)) != source_hash()
 
 
 def test_cpu_baseline_repeats_passes_and_names_them():

@@ -34,20 +34,25 @@ import os
 import re
 import statistics
 
-KERNEL_KEY = "attn_fwd_16_kernel<128, true, false, false, false, 8>"
+KERNEL_KEY = "attn_fwd_16_kernel<128, true, false, false, false, false>"
 COPY_BYTES = 256 * 1024 * 1024
 SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "tileattn.hip")
+# Sources of the attention kernel that the recorded figures depend on.
+KERNEL_SOURCES = (SRC, os.path.join(os.path.dirname(SRC), "attn_common.h"))
 
 
-def source_hash(path: str = SRC) -> str:
-    """Hash of the kernel source with comments and whitespace removed: the
-    recorded figures stay valid across comment edits and go stale with any
-    change to the code itself."""
-    with open(path) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    return hashlib.sha256("".join(text.split()).encode()).hexdigest()[:16]
+def source_hash(*paths: str) -> str:
+    """Hash of the kernel sources (default: KERNEL_SOURCES) with comments and
+    whitespace removed: the recorded figures stay valid across comment edits
+    and go stale with any change to the code itself."""
+    h = hashlib.sha256()
+    for path in paths or KERNEL_SOURCES:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update("".join(text.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def _csv(d: str, suffix: str):
