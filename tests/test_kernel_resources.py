@@ -26,7 +26,6 @@ BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 # attn_fwd_16_kernel<D, CAUSAL, IS_F16, MASK, ALIBI, SPLIT>
 SPILL_BOUNDS = [
     (r"attn_fwd_16_kernelILi128ELb[01]ELb[01]ELb[01]ELb1ELb0E", 64),   # D = 128, linear bias
-    (r"attn_fwd_16_kernelILi128ELb[01]ELb[01]ELb0ELb0ELb1E", 80),      # D = 128, key split
 ]
 
 

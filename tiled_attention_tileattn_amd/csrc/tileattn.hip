@@ -358,21 +358,78 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   auto kslot = [&](int j) { return (2 * set + (j & 1)) * T::kKBytes; };
   auto vslot = [&](int j) { return T::kVOff + (2 * set + (j & 1)) * T::kVBytes; };
 
+  // The key split at D = 128 moves K and V rows from memory straight into
+  // LDS (buffer_load_dwordx4 with the LDS flag: 64 lanes x 16 bytes, lane l's
+  // bytes written at M0 + 16 l): staging registers for a whole tile per
+  // group would not fit beside the rest of the wave's state.  Slots keep
+  // their bases but hold unpadded 256-byte rows, a 16-byte chunk c of key r
+  // at chunk position c ^ (r & 15) in K and c ^ 4 (r & 3) in V: the 16 keys
+  // of one K-operand read phase (same chunk of consecutive keys) and the 4
+  // keys x 64 bytes of one transposed V read phase then cover all 64 banks,
+  // as the padded pitches do.  Each lane loads the global chunk its LDS
+  // position holds.  Wave w of a group moves 1 KiB pieces n = 4 (w & 3) + e
+  // (rows 4n to 4n + 3) of its group's tiles.  The loads are inline asm: the
+  // compiler would otherwise wait for every one of them before each LDS read
+  // (it cannot tell the rows from the operands).  They are the only
+  // vector-memory loads of the tile loop, and each wave waits for its own
+  // (vmcnt) before the barrier that publishes them.
+  constexpr bool kDma = SPLIT && D == 128;
+  constexpr int kRowBytes = D * 2;
+  constexpr int kDmaPieces = kBlockN * kRowBytes / 1024 / 4;  // per wave and tile
+  static_assert(!kDma || (kDmaPieces == 4 && kBlockN * kRowBytes <= T::kKBytes), "unpadded tile fits a slot");
+  const unsigned smem_base = (unsigned)(uintptr_t)smem;  // LDS byte address of smem
+  unsigned k_voff[kDma ? kDmaPieces : 1];
+  unsigned v_voff = 0;
+  if constexpr (kDma) {
+    const int row_in = lane >> 4, p = lane & 15;
+#pragma unroll
+    for (int e = 0; e < kDmaPieces; ++e) k_voff[e] = row_in * kRowBytes + ((p ^ (4 * e + row_in)) << 4);
+    v_voff = row_in * kRowBytes + ((p ^ (row_in << 2)) << 4);
+  }
+  auto dma_tile = [&](const __amdgpu_buffer_rsrc_t& rsrc, bool is_k, int t, int slot) {
+    const int tile_off = t * kBlockN * kRowBytes;
+#pragma unroll
+    for (int e = 0; e < kDmaPieces; ++e) {
+      const int n = (wave & 3) * kDmaPieces + e;  // n & 3 = e
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :: "s"(__builtin_amdgcn_readfirstlane(smem_base + slot + n * 1024)),
+                      "v"(is_k ? k_voff[e] : v_voff), "s"(rsrc),
+                      "s"(__builtin_amdgcn_readfirstlane(tile_off + n * 1024))
+                   : "memory", "m0");
+    }
+  };
+  auto dma_wait_all = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
   const int s16 = lane & 15;
   const int k_lane_off = l32 * T::kKPitch + 16 * half;
   const int v_lane_off = (4 * half + (s16 >> 2)) * T::kVPitch +
                          2 * (16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
 
+  // Swizzled slots: the lane's byte offset of K chunk 2a + half of its key
+  // (key & 15 = l32 & 15 for both 32-key halves), and of the transposed-read
+  // piece of V column group db (row & 3 = s16 >> 2 for every read).
+  unsigned kofs[kDma ? D / 16 : 1], vofs[kDma ? D / 32 : 1];
+  if constexpr (kDma) {
+#pragma unroll
+    for (int a = 0; a < D / 16; ++a) kofs[a] = l32 * kRowBytes + (((2 * a + half) ^ (l32 & 15)) << 4);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      vofs[db] = (4 * half + (s16 >> 2)) * kRowBytes + 64 * (db ^ (s16 >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (s16 & 3);
+  }
   auto k_operand = [&](int kbase, int i) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(smem + kbase + (i & 1) * 32 * T::kKPitch + (i >> 1) * 32);
+    if constexpr (kDma)
+      return *reinterpret_cast<const bf16x8*>(smem + kbase + kofs[i >> 1] + (i & 1) * 32 * kRowBytes);
+    else
+      return *reinterpret_cast<const bf16x8*>(smem + kbase + (i & 1) * 32 * T::kKPitch + (i >> 1) * 32);
   };
   auto v_operand = [&](int vbase, int i) -> bf16x8 {
     typedef short i16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     const int g = i / (D / 32), db = i % (D / 32);
-    const unsigned char* vs = smem + vbase + 16 * g * T::kVPitch + db * 64;
+    constexpr int kPitch = kDma ? kRowBytes : T::kVPitch;
+    const unsigned char* vs = kDma ? smem + vbase + vofs[db] + 16 * g * kPitch : smem + vbase + 16 * g * kPitch + db * 64;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)vs);
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vs + 8 * T::kVPitch));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vs + 8 * kPitch));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
@@ -398,7 +455,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   auto matrix_body = [&](auto with_s_c, auto with_pv_c, int j) {
     constexpr bool WITH_S = decltype(with_s_c)::value;
     constexpr bool WITH_PV = decltype(with_pv_c)::value;
-    const int kb = kslot(j) + k_lane_off, vb = vslot(j - 1) + v_lane_off;
+    const int kb = kslot(j) + (kDma ? 0 : k_lane_off), vb = vslot(j - 1) + (kDma ? 0 : v_lane_off);
     if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
     bf16x8 kring[kP], vring[kP];
 #pragma unroll
@@ -506,6 +563,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     if (ld_v) store_rows(vslot(j), T::kVPitch, vreg);
     __syncthreads();
   };
+  // LDS-direct version (key split at D = 128, both groups): K_{j+1} and V_j
+  // go into the slots that K_{j-1} and V_{j-2} left at the top of iteration
+  // j, and land before its closing barrier.
+  auto iteration_dma = [&](int j, auto first, auto second) {
+    if (j + 1 < nt) dma_tile(krsrc, true, tile(j + 1), kslot(j + 1));
+    if (j < nt) dma_tile(vrsrc, false, tile(j), vslot(j));
+    TILEATTN_CHECK_BARRIER();
+    first();
+    TILEATTN_CHECK_BARRIER();
+    __builtin_amdgcn_s_barrier();
+    second();
+    TILEATTN_CHECK_BARRIER();
+    dma_wait_all();
+    __syncthreads();
+  };
   auto iteration1 = [&](int j, auto first, auto second) {
     if (j + 1 < nt) store_rows(kslot(j + 1), T::kKPitch, kreg);
     if (j < nt) store_rows(vslot(j), T::kVPitch, vreg);
@@ -524,7 +596,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   // have no visible key (o = 0, lse = -inf below).
   if (!MASK || nt > 0) {
     if constexpr (ALIBI) bias_init(0);
-    load_rows(krsrc, tile(0), kreg);
+    if constexpr (kDma)
+      dma_tile(krsrc, true, tile(0), kslot(0));
+    else
+      load_rows(krsrc, tile(0), kreg);
     if (row_owner) {
 #pragma unroll
       for (int i = 0; i < T::kRowLoads; ++i) {
@@ -532,10 +607,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
         *reinterpret_cast<u32x4*>(stage + (idx / T::kChunks) * T::kKPitch + (idx % T::kChunks) * 16) = qreg[i];
       }
     }
-    store_rows(kslot(0), T::kKPitch, kreg);
-    if (SPLIT || group == 1) {
-      if (nt > 1) load_rows(krsrc, tile(1), kreg);
-      load_rows(vrsrc, tile(0), vreg);
+    if constexpr (kDma) {
+      dma_wait_all();
+    } else {
+      store_rows(kslot(0), T::kKPitch, kreg);
+      if (SPLIT || group == 1) {
+        if (nt > 1) load_rows(krsrc, tile(1), kreg);
+        load_rows(vrsrc, tile(0), vreg);
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -545,7 +624,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     // wave writes V_0 there.
     if constexpr (T::kStageOverV) __syncthreads();
 
-    if (group == 0 && SPLIT) {
+    if (kDma && group == 0) {
+      iteration_dma(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
+      for (int j = 1; j < nt; ++j)
+        iteration_dma(j, [&] { matrix_phase(TT{}, TT{}, j); }, [&] { vector_phase(j); });
+      iteration_dma(nt, [&] { matrix_phase(FF{}, TT{}, nt); }, [&] {});
+    } else if (kDma) {
+      iteration_dma(0, [&] {}, [&] { matrix_phase(TT{}, FF{}, 0); });
+      for (int j = 1; j < nt; ++j)
+        iteration_dma(j, [&] { vector_phase(j - 1); }, [&] { matrix_phase(TT{}, TT{}, j); });
+      iteration_dma(nt, [&] { vector_phase(nt - 1); }, [&] { matrix_phase(FF{}, TT{}, nt); });
+    } else if (group == 0 && SPLIT) {
       // Split: group 0 stages its own tiles one iteration ahead, as group 1
       // does (no other group writes half of them).
       iteration1(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
