@@ -1,12 +1,12 @@
 """Register spills of the built kernels (CPU only: reads the code-object
 metadata of ``libtileattn.so`` with ``llvm-readelf``, runs nothing).
 
-Every kernel holds its working set in registers, except two families of
-16-bit attention instances with D = 128 that spill a few registers: the
-linear-bias (ALiBi) instances, whose bias terms add to the staged K/V rows,
-and the key-split instances, whose groups each stage a whole tile (twice the
-K/V chunks per thread of the 256-row kernel).  Their per-lane scratch is bounded here so that a change
-that spills more (or spills elsewhere) fails on the CPU."""
+Every kernel holds its working set in registers, except the 16-bit
+attention instances with D = 128 and a linear (ALiBi) bias, whose bias terms
+add to the staged K/V rows: they spill a few registers outside the tile
+loop.  Their per-lane scratch is bounded here, and every other kernel must
+have none, so that a change that spills more (or spills elsewhere) fails on
+the CPU."""
 
 import os
 import re
