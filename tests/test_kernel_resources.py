@@ -1,12 +1,8 @@
 """Register spills of the built kernels (CPU only: reads the code-object
 metadata of ``libtileattn.so`` with ``llvm-readelf``, runs nothing).
 
-Every kernel holds its working set in registers, except the 16-bit
-attention instances with D = 128 and a linear (ALiBi) bias, whose bias terms
-add to the staged K/V rows: they spill a few registers outside the tile
-loop.  Their per-lane scratch is bounded here, and every other kernel must
-have none, so that a change that spills more (or spills elsewhere) fails on
-the CPU."""
+Every kernel holds its working set in registers: no kernel may use
+scratch memory, so that a change that spills fails on the CPU."""
 
 import os
 import re
@@ -21,13 +17,6 @@ import tiled_attention_tileattn_amd as ta
 READELF = next((p for p in ("/opt/rocm/llvm/bin/llvm-readelf", shutil.which("llvm-readelf") or "")
                 if p and os.path.exists(p)), None)
 BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
-
-# (template-argument pattern of the mangled name, max bytes of scratch per lane)
-# attn_fwd_16_kernel<D, CAUSAL, IS_F16, MASK, ALIBI, SPLIT>
-SPILL_BOUNDS = [
-    (r"attn_fwd_16_kernelILi128ELb[01]ELb[01]ELb[01]ELb1ELb0E", 64),   # D = 128, linear bias
-]
-
 
 def _code_objects(path):
     """The gfx950 code objects of every offload bundle in the library's
@@ -65,9 +54,8 @@ def _kernel_scratch(tmp_path):
 
 
 @pytest.mark.skipif(READELF is None, reason="llvm-readelf (ROCm) not found")
-def test_kernels_spill_only_where_bounded(tmp_path):
+def test_no_kernel_spills(tmp_path):
     scratch = _kernel_scratch(tmp_path)
     assert any("attn_fwd_16_kernel" in n for n in scratch) and any("attn_fwd_f32_kernel" in n for n in scratch)
     for name, bytes_per_lane in scratch.items():
-        bound = next((b for pat, b in SPILL_BOUNDS if re.search(pat, name)), 0)
-        assert bytes_per_lane <= bound, f"{name}: {bytes_per_lane} B/lane of scratch (bound {bound})"
+        assert bytes_per_lane == 0, f"{name}: {bytes_per_lane} B/lane of scratch"

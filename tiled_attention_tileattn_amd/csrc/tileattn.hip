@@ -358,39 +358,45 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   auto kslot = [&](int j) { return (2 * set + (j & 1)) * T::kKBytes; };
   auto vslot = [&](int j) { return T::kVOff + (2 * set + (j & 1)) * T::kVBytes; };
 
-  // The key split at D = 128 moves K and V rows from memory straight into
-  // LDS (buffer_load_dwordx4 with the LDS flag: 64 lanes x 16 bytes, lane l's
-  // bytes written at M0 + 16 l): staging registers for a whole tile per
-  // group would not fit beside the rest of the wave's state.  Slots keep
+  // The key split and the linear-bias instances at D = 128 move K and V rows
+  // from memory straight into LDS (buffer_load_dwordx4 with the LDS flag: 64
+  // lanes x 16 bytes, lane l's bytes written at M0 + 16 l): staging
+  // registers (for a whole tile per group, or beside the bias terms) would
+  // not fit beside the rest of the wave's state.  Slots keep
   // their bases but hold unpadded 256-byte rows, a 16-byte chunk c of key r
   // at chunk position c ^ (r & 15) in K and c ^ 4 (r & 3) in V: the 16 keys
   // of one K-operand read phase (same chunk of consecutive keys) and the 4
   // keys x 64 bytes of one transposed V read phase then cover all 64 banks,
   // as the padded pitches do.  Each lane loads the global chunk its LDS
-  // position holds.  Wave w of a group moves 1 KiB pieces n = 4 (w & 3) + e
-  // (rows 4n to 4n + 3) of its group's tiles.  The loads are inline asm: the
+  // position holds.  The waves that stage a tile (a group's four when split,
+  // else all eight) move its 1 KiB pieces n (rows 4n to 4n + 3) in turn.  The loads are inline asm: the
   // compiler would otherwise wait for every one of them before each LDS read
   // (it cannot tell the rows from the operands).  They are the only
   // vector-memory loads of the tile loop, and each wave waits for its own
   // (vmcnt) before the barrier that publishes them.
-  constexpr bool kDma = SPLIT && D == 128;
+  constexpr bool kDma = D == 128 && (SPLIT || ALIBI);
   constexpr int kRowBytes = D * 2;
-  constexpr int kDmaPieces = kBlockN * kRowBytes / 1024 / 4;  // per wave and tile
-  static_assert(!kDma || (kDmaPieces == 4 && kBlockN * kRowBytes <= T::kKBytes), "unpadded tile fits a slot");
+  constexpr int kDmaPieces = kBlockN * kRowBytes / 1024 / (SPLIT ? 4 : 8);  // per wave and tile
+  static_assert(!kDma || (kDmaPieces * 1024 * (SPLIT ? 4 : 8) == kBlockN * kRowBytes &&
+                          kBlockN * kRowBytes <= T::kKBytes), "whole pieces; unpadded tile fits a slot");
+  const int dma_wave = SPLIT ? (wave & 3) : wave;  // this wave's rank among a tile's stagers
   const unsigned smem_base = (unsigned)(uintptr_t)smem;  // LDS byte address of smem
   unsigned k_voff[kDma ? kDmaPieces : 1];
   unsigned v_voff = 0;
   if constexpr (kDma) {
     const int row_in = lane >> 4, p = lane & 15;
 #pragma unroll
-    for (int e = 0; e < kDmaPieces; ++e) k_voff[e] = row_in * kRowBytes + ((p ^ (4 * e + row_in)) << 4);
+    for (int e = 0; e < kDmaPieces; ++e) {
+      const int n = dma_wave * kDmaPieces + e;
+      k_voff[e] = row_in * kRowBytes + ((p ^ (4 * (n & 3) + row_in)) << 4);
+    }
     v_voff = row_in * kRowBytes + ((p ^ (row_in << 2)) << 4);
   }
   auto dma_tile = [&](const __amdgpu_buffer_rsrc_t& rsrc, bool is_k, int t, int slot) {
     const int tile_off = t * kBlockN * kRowBytes;
 #pragma unroll
     for (int e = 0; e < kDmaPieces; ++e) {
-      const int n = (wave & 3) * kDmaPieces + e;  // n & 3 = e
+      const int n = dma_wave * kDmaPieces + e;
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                    :: "s"(__builtin_amdgcn_readfirstlane(smem_base + slot + n * 1024)),
                       "v"(is_k ? k_voff[e] : v_voff), "s"(rsrc),
@@ -563,9 +569,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     if (ld_v) store_rows(vslot(j), T::kVPitch, vreg);
     __syncthreads();
   };
-  // LDS-direct version (key split at D = 128, both groups): K_{j+1} and V_j
-  // go into the slots that K_{j-1} and V_{j-2} left at the top of iteration
-  // j, and land before its closing barrier.
+  // LDS-direct version (both groups): K_{j+1} and V_j go into the slots that
+  // K_{j-1} and V_{j-2} left at the top of iteration j, and land before its
+  // closing barrier.
   auto iteration_dma = [&](int j, auto first, auto second) {
     if (j + 1 < nt) dma_tile(krsrc, true, tile(j + 1), kslot(j + 1));
     if (j < nt) dma_tile(vrsrc, false, tile(j), vslot(j));
