@@ -31,9 +31,11 @@
 //   * Q lives in VGPRs for the whole loop (B operand of the first product).
 //     It arrives, and O leaves, whole rows at a time through a per-wave LDS
 //     area, since in the MFMA layouts a lane holds only pieces of a row.
-//   * K and V tiles are double-buffered in LDS with padded row pitches (no
-//     bank conflicts); operands are read into a small register ring a few
-//     MFMAs ahead of use.
+//   * K and V tiles are double-buffered in LDS, laid out so that the operand
+//     reads have no bank conflicts: padded row pitches at D = 64, staged
+//     through registers; at D = 128 unpadded rows with an XOR swizzle of
+//     their 16-byte chunks, which buffer loads write straight into LDS.
+//     Operands are read into a small register ring a few MFMAs ahead of use.
 //   * Ping-pong: the waves of a SIMD alternate between a matrix phase (only
 //     MFMAs: the scores of tile j and the P*V update of tile j-1) and a
 //     vector phase (the online softmax), half a tile apart, so that one wave
@@ -221,7 +223,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     const float* __restrict__ slopes, const unsigned char* __restrict__ bmask, int mask_heads) {
   using T = Bf16Tile<D, SPLIT>;
   static_assert(T::kThreads == 512, "two groups of four waves");
-  static_assert(!SPLIT || (!MASK && !ALIBI), "the key split serves the plain kernel");
   __shared__ __attribute__((aligned(16)))
   unsigned char smem[T::kSmemBytes];
 
@@ -289,15 +290,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   // the first visible tile, so the lazy reference is rarely raised after it.
   constexpr bool kReversed = ALIBI && CAUSAL;
   auto order = [&](int j) -> int { return kReversed ? nt - 1 - j : j; };
-  // Key split: group g visits tiles g*h to g*h + h - 1 of the nkt, with
-  // h = ceil(nkt / 2).  When nkt is odd, group 1's last tile lies past the
-  // keys (past Sk, or past every row's diagonal): its loads read zeros, the
-  // mask hides every score, and it changes nothing.
-  const int tbase = SPLIT ? group * ((nkt + 1) / 2) : 0;
-  if (SPLIT) nt = (nkt + 1) / 2;
-  auto tile = [&](int j) -> int { return MASK ? (int)(tlist[order(j)] & 0xFFF) : tbase + order(j); };
+  // Key split: group g visits entries g*h to g*h + h - 1 of the nl tiles
+  // (the tile list with a block mask, else tiles 0 to nkt - 1), with
+  // h = ceil(nl / 2).  When nl is odd, group 1's last entry lies past the
+  // end: without a mask, a tile past the keys (past Sk, or past every row's
+  // diagonal), whose loads read zeros and whose scores the mask hides; with
+  // one, no list entry, which no wave sees.  Either way it changes nothing.
+  const int nl = nt;
+  const int lbase = SPLIT ? group * ((nl + 1) / 2) : 0;
+  if (SPLIT) nt = (nl + 1) / 2;
+  auto in_list = [&](int j) -> bool { return !SPLIT || lbase + order(j) < nl; };
+  auto tile = [&](int j) -> int {
+    if constexpr (MASK)
+      return in_list(j) ? (int)(tlist[lbase + order(j)] & 0xFFF) : nkt;
+    else
+      return lbase + order(j);
+  };
   // This wave's 64-row query block may see tile j (block mask).
-  auto wave_sees = [&](int j) -> bool { return !MASK || ((tlist[order(j)] >> (12 + (wave >> 1))) & 1); };
+  auto wave_sees = [&](int j) -> bool {
+    return !MASK || (in_list(j) && ((tlist[lbase + order(j)] >> (12 + (rw >> 1))) & 1));
+  };
 
   // With the bias, scores are kept in units of 1/kscale: the S product
   // starts from bias/kscale instead of 0 (see bias_init), so the softmax and
@@ -327,10 +339,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   }
   bf16x8 qf[D / 16];
 
-  // ---- tile loaders: global -> registers -> LDS ---------------------------
+  // ---- tile loaders ---------------------------------------------------------
   // Buffer loads over this head's K and V: the tile offset is a scalar, the
   // per-thread offset a constant, and rows past Sk fall outside the buffer
-  // range and read as 0 (those keys are masked).
+  // range and read as 0 (those keys are masked).  D = 64 stages them through
+  // registers into padded LDS rows (load_rows, store_rows); D = 128 loads
+  // them straight into LDS (dma_tile below).
   const int kv_bytes = Sk * D * 2;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, 0, kv_bytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, 0, kv_bytes, kBufferFlags);
@@ -358,11 +372,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   auto kslot = [&](int j) { return (2 * set + (j & 1)) * T::kKBytes; };
   auto vslot = [&](int j) { return T::kVOff + (2 * set + (j & 1)) * T::kVBytes; };
 
-  // The key split and the linear-bias instances at D = 128 move K and V rows
-  // from memory straight into LDS (buffer_load_dwordx4 with the LDS flag: 64
-  // lanes x 16 bytes, lane l's bytes written at M0 + 16 l): staging
-  // registers (for a whole tile per group, or beside the bias terms) would
-  // not fit beside the rest of the wave's state.  Slots keep
+  // At D = 128 K and V rows go from memory straight into LDS
+  // (buffer_load_dwordx4 with the LDS flag: 64 lanes x 16 bytes, lane l's
+  // bytes written at M0 + 16 l), with no staging registers (for the key
+  // split's whole tile per group, or beside the bias terms, they would not
+  // fit beside the rest of the wave's state) and no LDS-write instructions.  Slots keep
   // their bases but hold unpadded 256-byte rows, a 16-byte chunk c of key r
   // at chunk position c ^ (r & 15) in K and c ^ 4 (r & 3) in V: the 16 keys
   // of one K-operand read phase (same chunk of consecutive keys) and the 4
@@ -374,7 +388,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   // (it cannot tell the rows from the operands).  They are the only
   // vector-memory loads of the tile loop, and each wave waits for its own
   // (vmcnt) before the barrier that publishes them.
-  constexpr bool kDma = D == 128 && (SPLIT || ALIBI);
+  constexpr bool kDma = D == 128;
   constexpr int kRowBytes = D * 2;
   constexpr int kDmaPieces = kBlockN * kRowBytes / 1024 / (SPLIT ? 4 : 8);  // per wave and tile
   static_assert(!kDma || (kDmaPieces * 1024 * (SPLIT ? 4 : 8) == kBlockN * kRowBytes &&
@@ -977,15 +991,15 @@ int launch_waves(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16
 }
 
 // bf16 and fp16 inputs share one kernel template (IS_F16); a block mask and
-// the linear bias select the MASK / ALIBI instances (always 256-row).
+// the linear bias select the MASK / ALIBI instances.
 template <int D, bool IS_F16, bool MASK, bool ALIBI>
 int launch_variant(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
                    int B, int Hq, int Hkv, int Sq, int Sk, float scale, int causal,
                    const float* slopes, const unsigned char* bmask, int mask_heads, void* stream) {
-  if constexpr (!MASK && !ALIBI)
-    if (use_split(B, Hq, Sq))
-      return launch_waves<D, IS_F16, MASK, ALIBI, true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, causal,
-                                                        slopes, bmask, mask_heads, stream);
+  // Small grids take the key split.
+  if (use_split(B, Hq, Sq))
+    return launch_waves<D, IS_F16, MASK, ALIBI, true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, causal,
+                                                      slopes, bmask, mask_heads, stream);
   return launch_waves<D, IS_F16, MASK, ALIBI, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, causal,
                                                      slopes, bmask, mask_heads, stream);
 }
