@@ -16,15 +16,18 @@
 //   * the MFMA computes transposed blocks, C^T = B^T A^T: with B as the first
 //     operand a lane ends up owning 4 consecutive columns of C per register
 //     group, so the epilogue writes 16-byte (fp32) or 8-byte (bf16) pieces;
-//   * K steps of 64: the next A and B tiles are loaded with buffer loads into
-//     registers at the top of a step, the current tiles are multiplied out
-//     of LDS, and the registers are written to the other LDS slot between
-//     the MFMA blocks of the step's middle sub-steps (double buffering, one
-//     barrier per step);
+//   * K steps of 64: the next A and B tiles go from memory straight into the
+//     other LDS slot at the top of a step (buffer_load_dwordx4 with the LDS
+//     flag: 64 lanes x 16 bytes written at M0 + 16 * lane), while the current
+//     tiles are multiplied out of LDS (double buffering, one barrier per
+//     step);
 //   * A operand fragments are 16-byte LDS reads along K; B fragments are read
 //     down the columns of the row-major B tile with ds_read_b64_tr_b16;
-//   * padded LDS rows (A: 144 B, B: 576 B) make every operand read phase
-//     bank-conflict free;
+//   * LDS rows are unpadded (A: 128 B, B: 512 B, as the 1 KiB loads write
+//     them) and their 16-byte chunks XOR-swizzled so that every operand read
+//     phase is bank-conflict free: chunk c of A row r sits at position
+//     c ^ ((r >> 1) & 7), chunk c of B row r at c ^ 4 (r & 3); each lane
+//     loads the global chunk its LDS position holds;
 //   * ragged edges: each workgroup's buffer starts at its own tile, so rows
 //     past M (A) and K (B) fall outside the buffer's range and read as 0;
 //     column chunks past N (B) and past K (A, last step) get an offset
@@ -45,13 +48,13 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kThreads = 512;                 // 8 waves: 2 along M x 4 along N
 constexpr int kWaveM = 128, kWaveN = 64;
-constexpr int kAPitch = kBK * 2 + 16;         // bytes per A row in LDS
-constexpr int kBPitch = kBN * 2 + 64;         // bytes per B row in LDS
+constexpr int kAPitch = kBK * 2;              // bytes per A row in LDS
+constexpr int kBPitch = kBN * 2;              // bytes per B row in LDS
 constexpr int kABytes = kBM * kAPitch;
 constexpr int kBBytes = kBK * kBPitch;
 constexpr int kStage = kABytes + kBBytes;
-constexpr int kLoads = kBM * kBK / 8 / kThreads;  // 16-byte loads per thread per tile
-static_assert(kLoads == 4 && kBK * kBN / 8 / kThreads == 4, "tile / thread count mismatch");
+constexpr int kPieces = kABytes / 1024 / (kThreads / 64);  // 1 KiB loads per wave per tile
+static_assert(kPieces == 4 && kBBytes / 1024 / (kThreads / 64) == 4, "tile / wave count mismatch");
 constexpr unsigned kOutOfRange = 0x80000000u;  // beyond any buffer range used here
 constexpr int kBufferFlags = 0x00020000;
 #ifndef TILEATTN_MM_GROUP
@@ -97,23 +100,37 @@ __global__ __launch_bounds__(kThreads) void matmul_bf16_kernel(const uint16_t* A
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int nk = (K + kBK - 1) / kBK;
 
-  // Per-thread load offsets.  A chunk i: row idx/8, 16-byte chunk idx%8 of the
-  // 64-wide K slice; B chunk i: row idx/32, chunk idx%32 of the 256 columns.
-  int a_off[kLoads], a_col[kLoads], b_off[kLoads];
+  // Tile loads.  Wave w moves the 1 KiB pieces n = 4w + e (e = 0..3) of each
+  // tile: A rows 8n .. 8n + 7 (lane: row 8n + lane / 8, chunk position
+  // lane % 8), B rows 2n, 2n + 1 (lane: row 2n + lane / 32, position
+  // lane % 32).  The lane's byte offset in the tile is its global chunk's:
+  // the swizzle is applied on the load side.  A chunks past K (last step)
+  // and B chunks past N get an offset outside the buffer range (zeros).
+  int a_off[kPieces], a_col[kPieces], b_off[kPieces];
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int idx = tid + i * kThreads;
-    const int ar = idx >> 3, ac = idx & 7;
-    a_off[i] = ar * K * 2 + ac * 16;
-    a_col[i] = ac * 8;
-    const int br = idx >> 5, bc = idx & 31;
-    b_off[i] = (n0 + bc * 8 < N) ? br * N * 2 + bc * 16 : (int)kOutOfRange;
+  for (int e = 0; e < kPieces; ++e) {
+    const int n = wave * kPieces + e;
+    const int ar = 8 * n + (lane >> 3);
+    const int ac = (lane & 7) ^ ((ar >> 1) & 7);
+    a_off[e] = ar * K * 2 + ac * 16;
+    a_col[e] = ac * 8;
+    const int br = 2 * n + (lane >> 5);
+    const int bc = (lane & 31) ^ (4 * (br & 3));
+    b_off[e] = (n0 + bc * 8 < N) ? br * N * 2 + bc * 16 : (int)kOutOfRange;
   }
   const long long a_rows_bytes = (long long)(M - m0) * K * 2;
   const long long b_rows_bytes = (long long)K * N * 2 - (long long)n0 * 2;
+  const unsigned smem_base = (unsigned)(uintptr_t)smem;  // LDS byte address of smem
 
-  u32x4 areg[kLoads], breg[kLoads];
-  auto load_tiles = [&](int kt) {
+  // The loads are inline asm: the compiler would otherwise wait for every one
+  // of them before each LDS read.  They are the kernel's only vector-memory
+  // loads; each wave waits for its own (vmcnt) before the step's closing
+  // barrier.
+  auto dma = [&](const __amdgpu_buffer_rsrc_t& r, int voff, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r) : "memory", "m0");
+  };
+  auto load_tiles = [&](int kt, int stage) {
     const int k0 = kt * kBK;
     const long long na = a_rows_bytes - (long long)k0 * 2;
     const long long nb = b_rows_bytes - (long long)k0 * N * 2;
@@ -123,42 +140,41 @@ __global__ __launch_bounds__(kThreads) void matmul_bf16_kernel(const uint16_t* A
         (void*)(B + (size_t)k0 * N + n0), 0, (int)min(nb, (long long)INT_MAX), kBufferFlags);
     const bool k_edge = k0 + kBK > K;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int off = (k_edge && a_col[i] >= K - k0) ? (int)kOutOfRange : a_off[i];
-      areg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
-      breg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[i], 0, 0));
+    for (int e = 0; e < kPieces; ++e) {
+      const int n = wave * kPieces + e;
+      const int off = (k_edge && a_col[e] >= K - k0) ? (int)kOutOfRange : a_off[e];
+      dma(ra, off, smem_base + stage + n * 1024);
+      dma(rb, b_off[e], smem_base + stage + kABytes + n * 1024);
     }
   };
-  auto store_a = [&](int stage) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int idx = tid + i * kThreads;
-      *reinterpret_cast<u32x4*>(smem + stage + (idx >> 3) * kAPitch + (idx & 7) * 16) = areg[i];
-    }
-  };
-  auto store_b = [&](int stage) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int idx = tid + i * kThreads;
-      *reinterpret_cast<u32x4*>(smem + stage + kABytes + (idx >> 5) * kBPitch + (idx & 31) * 16) = breg[i];
-    }
-  };
+  auto dma_wait = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // Operand fragments.  A: lane (row l32, k half) reads 8 consecutive k of
   // one row.  B: ds_read_b64_tr_b16 hands output lane 4a+b of each 16-lane
   // group element b of source lanes a, a+4, a+8, a+12; source lane s reads 4
   // columns 4(s%4).. of k-row s/4, so a lane receives 4 consecutive k of one
   // column, and the second read (4 rows further) the next 4.
-  const int a_lane = (wm * kWaveM + l32) * kAPitch + half * 16;
-  const int b_lane = kABytes + (8 * half + (s16 >> 2)) * kBPitch +
-                     2 * (wn * kWaveN + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
+  // With the swizzle: A row wm*128 + mb*32 + l32 has (row >> 1) & 7 =
+  // (l32 >> 1) & 7, so the lane's offset of k chunk 2t + half is aofs[t]
+  // plus an immediate per mb; B row 16t + 8*half + s16/4 (+4) has row & 3 =
+  // s16 >> 2, and the lane's 64-byte column group 2*(wn & 1) + nb of the
+  // 256-byte half wn >> 1 moves by XOR with it: bofs[nb] plus an immediate
+  // per t.
+  int aofs[kBK / 16], bofs[2];
+#pragma unroll
+  for (int t = 0; t < kBK / 16; ++t)
+    aofs[t] = (wm * kWaveM + l32) * kAPitch + (((2 * t + half) ^ ((l32 >> 1) & 7)) << 4);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+    bofs[nb] = kABytes + (8 * half + (s16 >> 2)) * kBPitch + 256 * (wn >> 1) +
+               64 * ((2 * (wn & 1) + nb) ^ (s16 >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (s16 & 3);
   auto a_frag = [&](int base, int mb, int t) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(smem + base + mb * 32 * kAPitch + t * 32);
+    return *reinterpret_cast<const bf16x8*>(smem + base + aofs[t] + mb * 32 * kAPitch);
   };
   auto b_frag = [&](int base, int nb, int t) -> bf16x8 {
     typedef short i16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const unsigned char* p = smem + base + t * 16 * kBPitch + nb * 64;
+    const unsigned char* p = smem + base + bofs[nb] + t * 16 * kBPitch;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p);
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p + 4 * kBPitch));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -171,16 +187,17 @@ __global__ __launch_bounds__(kThreads) void matmul_bf16_kernel(const uint16_t* A
     for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x16{};
 
   if (nk > 0) {
-    load_tiles(0);
-    store_a(0);
-    store_b(0);
+    load_tiles(0, 0);
+    dma_wait();
     __syncthreads();
   }
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_tiles(kt + 1);
+    // The other slot was last read in the previous step, before its closing
+    // barrier.
+    if (kt + 1 < nk) load_tiles(kt + 1, ((kt + 1) & 1) * kStage);
     int stage = (kt & 1) * kStage;
     asm volatile("" : "+s"(stage));  // one runtime base: operand addresses stay base + immediate
-    const int abase = stage + a_lane, bbase = stage + b_lane;
+    const int abase = stage, bbase = stage;
     bf16x8 af[2][4], bfr[2][2];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) af[0][mb] = a_frag(abase, mb, 0);
@@ -199,12 +216,8 @@ __global__ __launch_bounds__(kThreads) void matmul_bf16_kernel(const uint16_t* A
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma(bfr[cur][nb], af[cur][mb], acc[nb][mb]);
-      // The staged next tile goes to the other slot (last read in the
-      // previous step, before its closing barrier) between the MFMA blocks of
-      // the middle sub-steps, A after the second and B after the third.
-      if (kt + 1 < nk && t == 1) store_a(((kt + 1) & 1) * kStage);
-      if (kt + 1 < nk && t == 2) store_b(((kt + 1) & 1) * kStage);
     }
+    dma_wait();
     __syncthreads();
   }
 
