@@ -31,11 +31,11 @@
 //   * Q lives in VGPRs for the whole loop (B operand of the first product).
 //     It arrives, and O leaves, whole rows at a time through a per-wave LDS
 //     area, since in the MFMA layouts a lane holds only pieces of a row.
-//   * K and V tiles are double-buffered in LDS, laid out so that the operand
-//     reads have no bank conflicts: padded row pitches at D = 64, staged
-//     through registers; at D = 128 unpadded rows with an XOR swizzle of
-//     their 16-byte chunks, which buffer loads write straight into LDS.
-//     Operands are read into a small register ring a few MFMAs ahead of use.
+//   * K and V tiles are double-buffered in LDS as unpadded rows with an XOR
+//     swizzle of their 16-byte chunks, which makes the operand reads free of
+//     bank conflicts; buffer loads write them straight into LDS (no staging
+//     registers).  Operands are read into a small register ring a few MFMAs
+//     ahead of use.
 //   * Ping-pong: the waves of a SIMD alternate between a matrix phase (only
 //     MFMAs: the scores of tile j and the P*V update of tile j-1) and a
 //     vector phase (the online softmax), half a tile apart, so that one wave
@@ -98,32 +98,25 @@ struct Bf16Tile {
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kRowWaves = SPLIT ? kWaves / 2 : kWaves;  // waves with distinct query rows
   static constexpr int kBlockM = kRowWaves * kRowsPerWave;      // query rows per workgroup
-  static constexpr int kStagers = SPLIT ? kThreads / 2 : kThreads;  // threads staging one tile
   static constexpr int kSets = SPLIT ? 2 : 1;                    // K/V slot pairs (one per group)
   static constexpr int kChunks = D / 8;                    // 16-byte chunks per K/V row
-  // LDS row pitches (bytes).  K rows are padded by 16 bytes: the 16 rows of
-  // one K-operand read phase (same 16-byte chunk of consecutive keys) then
-  // start 16 bytes apart modulo 256 and hit distinct banks.  V rows are
-  // padded by 64 bytes: one phase of the transposed V read touches 4
-  // consecutive keys x 64 contiguous bytes, which then tile 256 bytes
-  // exactly.  Padding (rather than an XOR swizzle) keeps every operand
-  // address of a lane a compile-time offset from one base register.
-  static constexpr int kKPitch = D * 2 + 16;
-  static constexpr int kVPitch = D * 2 + 64;
-  static constexpr int kKBytes = kBlockN * kKPitch;
-  static constexpr int kVBytes = kBlockN * kVPitch;
-  static constexpr int kLoads = kBlockN * kChunks / kStagers;  // 16-byte loads per tensor
-  static_assert(kLoads >= 1 && kLoads * kStagers == kBlockN * kChunks, "tile/threads mismatch");
+  // A slot holds one tile's 64 unpadded rows (D * 2 bytes each, chunks
+  // swizzled; see the kernel's tile loaders).  K slots are 16 bytes a row
+  // larger: room that lets the split kernel's merge area (64 (D/2 + 2)
+  // floats per row pair, over the K slots) fit.
+  static constexpr int kKBytes = kBlockN * (D * 2 + 16);
+  static constexpr int kVBytes = kBlockN * D * 2;
   // Per-wave staging area for Q on the way in and O on the way out: the
-  // wave's 32 rows at the K pitch, so the operand-layout reads of Q are
-  // conflict-free like those of K.
+  // wave's 32 rows padded by 16 bytes, so the 16 rows of one operand-layout
+  // read phase of Q start 16 bytes apart modulo 256 and hit distinct banks.
+  static constexpr int kKPitch = D * 2 + 16;
   static constexpr int kStageBytes = kRowsPerWave * kKPitch;
   static constexpr int kRowLoads = kRowsPerWave * kChunks / 64;  // 16-byte chunks per lane
   // LDS layout: K slots 0 and 1, V slots 0 and 1, then the staging areas
   // (one per row wave).  The split kernel has two such slot pairs per tensor
   // (set g for group g) and lays its staging areas over the V slots instead
   // (Q is staged before the first V tile is written, O after the last one is
-  // read), which keeps it within 148 KiB at D = 128.
+  // read), which keeps it within 132 KiB at D = 128.
   static constexpr bool kStageOverV = SPLIT;
   static constexpr int kVOff = kSets * 2 * kKBytes;
   static constexpr int kStageOff = kVOff + (kStageOverV ? 0 : kSets * 2 * kVBytes);
@@ -340,71 +333,58 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   bf16x8 qf[D / 16];
 
   // ---- tile loaders ---------------------------------------------------------
-  // Buffer loads over this head's K and V: the tile offset is a scalar, the
-  // per-thread offset a constant, and rows past Sk fall outside the buffer
-  // range and read as 0 (those keys are masked).  D = 64 stages them through
-  // registers into padded LDS rows (load_rows, store_rows); D = 128 loads
-  // them straight into LDS (dma_tile below).
+  // K and V rows go from memory straight into LDS (buffer_load_dwordx4 with
+  // the LDS flag: 64 lanes x 16 bytes, lane l's bytes written at M0 + 16 l),
+  // 1 KiB per instruction, with no staging registers and no LDS-write
+  // instructions.  The loads are buffer loads over this head's K or V: rows
+  // past Sk fall outside the buffer range and arrive as 0 (those keys are
+  // masked).  The slots hold unpadded rows (D * 2 bytes) with their 16-byte
+  // chunks XOR-swizzled, so that the operand reads have no bank conflicts
+  // (64 banks x 4 bytes = one 256-byte line, holding kRowsPerLine rows):
+  //   * K: chunk c of key r sits at position c ^ kswz(r).  The 16 lanes of
+  //     one operand-read phase read the same chunk of 16 consecutive keys,
+  //     which then land in 16 distinct 16-byte slots of a line;
+  //   * V: chunk c of key r sits at c ^ vswz(r), which moves the 64-byte
+  //     column groups: one transposed-read phase reads 4 consecutive keys x
+  //     64 bytes, which then cover a line.
+  // Each lane loads the global chunk its LDS position holds.  The waves that
+  // stage a tile (a group's four in the key split, else all eight) move its
+  // pieces n (rows (1024 / kRowBytes) n on) in turn.  The loads are inline
+  // asm: the compiler would otherwise wait for every one of them before each
+  // LDS read (it cannot tell the rows from the operands).  They are the only
+  // vector-memory loads of the tile loop, and each wave waits for its own
+  // (vmcnt) before the barrier that publishes them.
+  constexpr int kRowBytes = D * 2;
+  constexpr int kChunksRow = kRowBytes / 16;       // 16-byte chunks per row: 16 or 8
+  constexpr int kRowsPerLine = 16 / kChunksRow;    // rows per 256-byte bank line: 1 or 2
+  constexpr int kRowsPiece = 1024 / kRowBytes;     // rows per 1 KiB load
+  constexpr int kStagers = SPLIT ? 4 : 8;          // waves staging one tile
+  constexpr int kDmaPieces = kBlockN * kRowBytes / 1024 / kStagers;  // per wave and tile
+  static_assert(kDmaPieces >= 1 && kDmaPieces * 1024 * kStagers == kBlockN * kRowBytes &&
+                kBlockN * kRowBytes <= T::kKBytes && kBlockN * kRowBytes <= T::kVBytes,
+                "whole pieces; an unpadded tile fits a slot");
+  auto kswz = [](int r) { return (r / kRowsPerLine) & (kChunksRow - 1); };
+  auto vswz = [](int r) { return 4 * ((r / kRowsPerLine) & (4 / kRowsPerLine - 1)); };
   const int kv_bytes = Sk * D * 2;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, 0, kv_bytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, 0, kv_bytes, kBufferFlags);
-  u32x4 kreg[T::kLoads], vreg[T::kLoads];
-  // Split: each group stages its own tiles (thread tid & 255 of the group).
-  const int stid = SPLIT ? (tid & 255) : tid;
-  auto load_rows = [&](const __amdgpu_buffer_rsrc_t& rsrc, int j, u32x4 (&reg)[T::kLoads]) {
-    const int tile_off = j * kBlockN * D * 2;
-#pragma unroll
-    for (int i = 0; i < T::kLoads; ++i) {
-      const int idx = stid + i * T::kStagers;
-      const int r = idx / T::kChunks, cc = idx % T::kChunks;
-      reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (r * D + cc * 8) * 2, tile_off, 0));
-    }
-  };
-  auto store_rows = [&](int byte0, int pitch, const u32x4 (&reg)[T::kLoads]) {
-#pragma unroll
-    for (int i = 0; i < T::kLoads; ++i) {
-      const int idx = stid + i * T::kStagers;
-      const int r = idx / T::kChunks, cc = idx % T::kChunks;
-      *reinterpret_cast<u32x4*>(smem + byte0 + r * pitch + cc * 16) = reg[i];
-    }
-  };
   const int set = SPLIT ? group : 0;  // this group's slot pair
   auto kslot = [&](int j) { return (2 * set + (j & 1)) * T::kKBytes; };
   auto vslot = [&](int j) { return T::kVOff + (2 * set + (j & 1)) * T::kVBytes; };
-
-  // At D = 128 K and V rows go from memory straight into LDS
-  // (buffer_load_dwordx4 with the LDS flag: 64 lanes x 16 bytes, lane l's
-  // bytes written at M0 + 16 l), with no staging registers (for the key
-  // split's whole tile per group, or beside the bias terms, they would not
-  // fit beside the rest of the wave's state) and no LDS-write instructions.  Slots keep
-  // their bases but hold unpadded 256-byte rows, a 16-byte chunk c of key r
-  // at chunk position c ^ (r & 15) in K and c ^ 4 (r & 3) in V: the 16 keys
-  // of one K-operand read phase (same chunk of consecutive keys) and the 4
-  // keys x 64 bytes of one transposed V read phase then cover all 64 banks,
-  // as the padded pitches do.  Each lane loads the global chunk its LDS
-  // position holds.  The waves that stage a tile (a group's four when split,
-  // else all eight) move its 1 KiB pieces n (rows 4n to 4n + 3) in turn.  The loads are inline asm: the
-  // compiler would otherwise wait for every one of them before each LDS read
-  // (it cannot tell the rows from the operands).  They are the only
-  // vector-memory loads of the tile loop, and each wave waits for its own
-  // (vmcnt) before the barrier that publishes them.
-  constexpr bool kDma = D == 128;
-  constexpr int kRowBytes = D * 2;
-  constexpr int kDmaPieces = kBlockN * kRowBytes / 1024 / (SPLIT ? 4 : 8);  // per wave and tile
-  static_assert(!kDma || (kDmaPieces * 1024 * (SPLIT ? 4 : 8) == kBlockN * kRowBytes &&
-                          kBlockN * kRowBytes <= T::kKBytes), "whole pieces; unpadded tile fits a slot");
   const int dma_wave = SPLIT ? (wave & 3) : wave;  // this wave's rank among a tile's stagers
   const unsigned smem_base = (unsigned)(uintptr_t)smem;  // LDS byte address of smem
-  unsigned k_voff[kDma ? kDmaPieces : 1];
-  unsigned v_voff = 0;
-  if constexpr (kDma) {
-    const int row_in = lane >> 4, p = lane & 15;
+  // The lane's byte offset in piece e: row row_in of the piece, the global
+  // chunk that its position p holds.  vswz of a piece's rows does not depend
+  // on the piece (a piece starts at a multiple of 4 lines' rows).
+  unsigned k_voff[kDmaPieces], v_voff;
+  {
+    const int row_in = lane / kChunksRow, p = lane % kChunksRow;
 #pragma unroll
     for (int e = 0; e < kDmaPieces; ++e) {
-      const int n = dma_wave * kDmaPieces + e;
-      k_voff[e] = row_in * kRowBytes + ((p ^ (4 * (n & 3) + row_in)) << 4);
+      const int r = (dma_wave * kDmaPieces + e) * kRowsPiece + row_in;
+      k_voff[e] = row_in * kRowBytes + ((p ^ kswz(r)) << 4);
     }
-    v_voff = row_in * kRowBytes + ((p ^ (row_in << 2)) << 4);
+    v_voff = row_in * kRowBytes + ((p ^ vswz(row_in)) << 4);
   }
   auto dma_tile = [&](const __amdgpu_buffer_rsrc_t& rsrc, bool is_k, int t, int slot) {
     const int tile_off = t * kBlockN * kRowBytes;
@@ -420,36 +400,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   };
   auto dma_wait_all = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
+  // Operand addresses.  K: lane (l32, half) reads chunk 2a + half of key
+  // 32 (i & 1) + l32 for MFMA i (a = i / 2); kswz of that key is kswz(l32).
+  // V: lane reads rows 16 g + 4 half + s16 / 4 (+ 8) at column group db,
+  // 32 ((lane >> 4) & 1) + 8 (s16 & 3) bytes in; vswz of those rows is
+  // vswz(4 half + s16 / 4).  Offsets per chunk pair and column group, the
+  // rest immediates.
   const int s16 = lane & 15;
-  const int k_lane_off = l32 * T::kKPitch + 16 * half;
-  const int v_lane_off = (4 * half + (s16 >> 2)) * T::kVPitch +
-                         2 * (16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
-
-  // Swizzled slots: the lane's byte offset of K chunk 2a + half of its key
-  // (key & 15 = l32 & 15 for both 32-key halves), and of the transposed-read
-  // piece of V column group db (row & 3 = s16 >> 2 for every read).
-  unsigned kofs[kDma ? D / 16 : 1], vofs[kDma ? D / 32 : 1];
-  if constexpr (kDma) {
+  unsigned kofs[D / 16], vofs[D / 32];
 #pragma unroll
-    for (int a = 0; a < D / 16; ++a) kofs[a] = l32 * kRowBytes + (((2 * a + half) ^ (l32 & 15)) << 4);
+  for (int a = 0; a < D / 16; ++a) kofs[a] = l32 * kRowBytes + (((2 * a + half) ^ kswz(l32)) << 4);
+  {
+    const int vr = 4 * half + (s16 >> 2);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
-      vofs[db] = (4 * half + (s16 >> 2)) * kRowBytes + 64 * (db ^ (s16 >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (s16 & 3);
+      vofs[db] = vr * kRowBytes + 64 * (db ^ (vswz(vr) >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (s16 & 3);
   }
   auto k_operand = [&](int kbase, int i) -> bf16x8 {
-    if constexpr (kDma)
-      return *reinterpret_cast<const bf16x8*>(smem + kbase + kofs[i >> 1] + (i & 1) * 32 * kRowBytes);
-    else
-      return *reinterpret_cast<const bf16x8*>(smem + kbase + (i & 1) * 32 * T::kKPitch + (i >> 1) * 32);
+    return *reinterpret_cast<const bf16x8*>(smem + kbase + kofs[i >> 1] + (i & 1) * 32 * kRowBytes);
   };
   auto v_operand = [&](int vbase, int i) -> bf16x8 {
     typedef short i16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     const int g = i / (D / 32), db = i % (D / 32);
-    constexpr int kPitch = kDma ? kRowBytes : T::kVPitch;
-    const unsigned char* vs = kDma ? smem + vbase + vofs[db] + 16 * g * kPitch : smem + vbase + 16 * g * kPitch + db * 64;
+    const unsigned char* vs = smem + vbase + vofs[db] + 16 * g * kRowBytes;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)vs);
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vs + 8 * kPitch));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vs + 8 * kRowBytes));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
@@ -475,7 +451,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   auto matrix_body = [&](auto with_s_c, auto with_pv_c, int j) {
     constexpr bool WITH_S = decltype(with_s_c)::value;
     constexpr bool WITH_PV = decltype(with_pv_c)::value;
-    const int kb = kslot(j) + (kDma ? 0 : k_lane_off), vb = vslot(j - 1) + (kDma ? 0 : v_lane_off);
+    const int kb = kslot(j), vb = vslot(j - 1);
     if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
     bf16x8 kring[kP], vring[kP];
 #pragma unroll
@@ -559,34 +535,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
 
   using TT = std::true_type;
   using FF = std::false_type;
-  // One iteration: loads of K_{j+1} and V_j at the top, the two halves, the
-  // stores into the slots no wave reads in this iteration, the closing barrier.
-  // Each group stages its own half of every tile's rows (thread tid covers
-  // chunks tid and tid + 512), and writes it to LDS while the other group runs
-  // its matrix phase, off the critical path:
-  //   group 0, iteration j: load K_{j+1}, V_j | M(j) | V(j), store them;
-  //   group 1, iteration j: store K_{j+1}, V_j (loaded one iteration
-  //     earlier), load K_{j+2}, V_{j+1} | V(j-1) | M(j).
-  // Both write the slots that K_{j-1} and V_{j-2} left; the closing barrier
-  // publishes the whole tile for iteration j+1.
-  auto iteration0 = [&](int j, auto first, auto second) {
-    const bool ld_k = j + 1 < nt, ld_v = j < nt;
-    if (ld_k) load_rows(krsrc, tile(j + 1), kreg);
-    if (ld_v) load_rows(vrsrc, tile(j), vreg);
-    TILEATTN_CHECK_BARRIER();
-    first();
-    TILEATTN_CHECK_BARRIER();
-    __builtin_amdgcn_s_barrier();
-    second();
-    TILEATTN_CHECK_BARRIER();
-    if (ld_k) store_rows(kslot(j + 1), T::kKPitch, kreg);
-    if (ld_v) store_rows(vslot(j), T::kVPitch, vreg);
-    __syncthreads();
-  };
-  // LDS-direct version (both groups): K_{j+1} and V_j go into the slots that
-  // K_{j-1} and V_{j-2} left at the top of iteration j, and land before its
-  // closing barrier.
-  auto iteration_dma = [&](int j, auto first, auto second) {
+  // One iteration (both groups): K_{j+1} and V_j go into the slots that
+  // K_{j-1} and V_{j-2} left at the top of iteration j, the two halves run,
+  // and the rows land before the closing barrier, which publishes them for
+  // iteration j+1.
+  auto iteration = [&](int j, auto first, auto second) {
     if (j + 1 < nt) dma_tile(krsrc, true, tile(j + 1), kslot(j + 1));
     if (j < nt) dma_tile(vrsrc, false, tile(j), vslot(j));
     TILEATTN_CHECK_BARRIER();
@@ -598,28 +551,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     dma_wait_all();
     __syncthreads();
   };
-  auto iteration1 = [&](int j, auto first, auto second) {
-    if (j + 1 < nt) store_rows(kslot(j + 1), T::kKPitch, kreg);
-    if (j < nt) store_rows(vslot(j), T::kVPitch, vreg);
-    if (j + 2 < nt) load_rows(krsrc, tile(j + 2), kreg);
-    if (j + 1 < nt) load_rows(vrsrc, tile(j + 1), vreg);
-    TILEATTN_CHECK_BARRIER();
-    first();
-    TILEATTN_CHECK_BARRIER();
-    __builtin_amdgcn_s_barrier();
-    second();
-    TILEATTN_CHECK_BARRIER();
-    __syncthreads();
-  };
 
   // A workgroup whose block mask shows it no tile skips the loop: its rows
   // have no visible key (o = 0, lse = -inf below).
   if (!MASK || nt > 0) {
     if constexpr (ALIBI) bias_init(0);
-    if constexpr (kDma)
-      dma_tile(krsrc, true, tile(0), kslot(0));
-    else
-      load_rows(krsrc, tile(0), kreg);
+    dma_tile(krsrc, true, tile(0), kslot(0));
     if (row_owner) {
 #pragma unroll
       for (int i = 0; i < T::kRowLoads; ++i) {
@@ -627,15 +564,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
         *reinterpret_cast<u32x4*>(stage + (idx / T::kChunks) * T::kKPitch + (idx % T::kChunks) * 16) = qreg[i];
       }
     }
-    if constexpr (kDma) {
-      dma_wait_all();
-    } else {
-      store_rows(kslot(0), T::kKPitch, kreg);
-      if (SPLIT || group == 1) {
-        if (nt > 1) load_rows(krsrc, tile(1), kreg);
-        load_rows(vrsrc, tile(0), vreg);
-      }
-    }
+    dma_wait_all();
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
@@ -644,33 +573,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     // wave writes V_0 there.
     if constexpr (T::kStageOverV) __syncthreads();
 
-    if (kDma && group == 0) {
-      iteration_dma(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
+    if (group == 0) {
+      iteration(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
       for (int j = 1; j < nt; ++j)
-        iteration_dma(j, [&] { matrix_phase(TT{}, TT{}, j); }, [&] { vector_phase(j); });
-      iteration_dma(nt, [&] { matrix_phase(FF{}, TT{}, nt); }, [&] {});
-    } else if (kDma) {
-      iteration_dma(0, [&] {}, [&] { matrix_phase(TT{}, FF{}, 0); });
-      for (int j = 1; j < nt; ++j)
-        iteration_dma(j, [&] { vector_phase(j - 1); }, [&] { matrix_phase(TT{}, TT{}, j); });
-      iteration_dma(nt, [&] { vector_phase(nt - 1); }, [&] { matrix_phase(FF{}, TT{}, nt); });
-    } else if (group == 0 && SPLIT) {
-      // Split: group 0 stages its own tiles one iteration ahead, as group 1
-      // does (no other group writes half of them).
-      iteration1(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
-      for (int j = 1; j < nt; ++j)
-        iteration1(j, [&] { matrix_phase(TT{}, TT{}, j); }, [&] { vector_phase(j); });
-      iteration1(nt, [&] { matrix_phase(FF{}, TT{}, nt); }, [&] {});
-    } else if (group == 0) {
-      iteration0(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
-      for (int j = 1; j < nt; ++j)
-        iteration0(j, [&] { matrix_phase(TT{}, TT{}, j); }, [&] { vector_phase(j); });
-      iteration0(nt, [&] { matrix_phase(FF{}, TT{}, nt); }, [&] {});
+        iteration(j, [&] { matrix_phase(TT{}, TT{}, j); }, [&] { vector_phase(j); });
+      iteration(nt, [&] { matrix_phase(FF{}, TT{}, nt); }, [&] {});
     } else {
-      iteration1(0, [&] {}, [&] { matrix_phase(TT{}, FF{}, 0); });
+      iteration(0, [&] {}, [&] { matrix_phase(TT{}, FF{}, 0); });
       for (int j = 1; j < nt; ++j)
-        iteration1(j, [&] { vector_phase(j - 1); }, [&] { matrix_phase(TT{}, TT{}, j); });
-      iteration1(nt, [&] { vector_phase(nt - 1); }, [&] { matrix_phase(FF{}, TT{}, nt); });
+        iteration(j, [&] { vector_phase(j - 1); }, [&] { matrix_phase(TT{}, TT{}, j); });
+      iteration(nt, [&] { vector_phase(nt - 1); }, [&] { matrix_phase(FF{}, TT{}, nt); });
     }
   }
 
