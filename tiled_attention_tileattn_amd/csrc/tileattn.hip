@@ -38,8 +38,10 @@
 //     ahead of use.
 //   * Ping-pong: the waves of a SIMD alternate between a matrix phase (only
 //     MFMAs: the scores of tile j and the P*V update of tile j-1) and a
-//     vector phase (the online softmax), half a tile apart, so that one wave
-//     keeps the matrix core busy while the other exponentiates.
+//     vector phase (the online softmax), half a tile apart (one group starts
+//     an iteration with its matrix phase, the other with its vector phase),
+//     so that one wave keeps the matrix core busy while the other
+//     exponentiates.
 //   * exp is computed as exp2 with scale*log2(e) folded into one FMA; the
 //     reference max is raised lazily, only when a tile's exponentials grow
 //     too large (see softmax_tile), which is exact.
@@ -55,9 +57,9 @@
 //   * Grids too small to fill the chip with 256-row workgroups take the key
 //     split instead: 128 query rows per workgroup, which both wave groups
 //     hold, each group running the same ping-pong over its own half of the
-//     key tiles (its own LDS slots, staged one tile ahead); at the end the
-//     two partial (acc, l, max) states of a row merge through LDS by the
-//     online-softmax update itself.
+//     key tiles (its own LDS slots); at the end the two partial
+//     (acc, l, max) states of a row merge through LDS by the online-softmax
+//     update itself.
 //   * Instances with a block mask compact the visible key tiles into an LDS
 //     list and skip, per wave, the tiles its rows cannot see; instances with
 //     a linear (ALiBi) bias start the score product from the bias, and walk
