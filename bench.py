@@ -393,6 +393,17 @@ def main():
             log(f"{HEADLINE} + {what}: median {t*1e6:.1f} us -> {flop/t/1e12:.1f} TFLOP/s "
                 f"on visible pairs ({flop/t/1e12/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
 
+        # One GPU's share of the headline if its KV heads were spread over
+        # Hkv GPUs (head sharding needs no communication): the same call on
+        # one KV head and its query heads.
+        from dataclasses import replace
+
+        sh = replace(w, name=f"{HEADLINE} head shard", Hq=w.Hq // w.Hkv, Hkv=1)
+        _, _, med, mn = time_workload(ta, sh, args.steps, args.warmup)
+        log(f"{HEADLINE}, one of {w.Hkv} head shards (B={sh.B}, Hq={sh.Hq}, Hkv=1): median "
+            f"{med*1e3:.1f} us min {mn*1e3:.1f} us -> {sh.flop()/med/1e9:.1f} TFLOP/s "
+            f"({sh.flop()/med/1e9/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
+
     w = WORKLOADS[HEADLINE]
     wall, mean, med, mn = time_workload(ta, w, args.steps, args.warmup)
     flop = w.flop()
