@@ -44,6 +44,8 @@
 #ifndef TILEATTN_H
 #define TILEATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -61,7 +63,8 @@ typedef enum {
                                   /* or Sk*D*4 > 2^31-1 (one head's K or V is read    */
                                   /* with 32-bit buffer offsets)                      */
   TILEATTN_ERR_LAUNCH = -8,       /* the HIP launch failed (e.g. no gfx950 device)    */
-  TILEATTN_ERR_DTYPE = -9         /* unknown tileattn_dtype code                      */
+  TILEATTN_ERR_DTYPE = -9,        /* unknown tileattn_dtype code                      */
+  TILEATTN_ERR_WORKSPACE = -10    /* workspace NULL or below the size it needs        */
 } tileattn_status;
 
 /* Storage type codes of tileattn_softmax and tileattn_gelu. */
@@ -133,6 +136,44 @@ int tileattn_fwd_ext(const void* q, const void* k, const void* v, void* o, float
                      float scale, int causal, const float* alibi_slopes,
                      const unsigned char* block_mask, int mask_heads, int is_f16,
                      void* stream);
+
+/*
+ * 16-bit attention forward with the key range of a query tile optionally
+ * split over several workgroups.  The online softmax of the page's step 6
+ * ("Flash Attention — Softmax Online") folds the tiles of a row one after
+ * another into (running max, running sum, accumulator); two such states over
+ * disjoint key ranges fold together by the same rescale-and-add, so a query
+ * tile's keys can be cut into chunks that run in parallel and are merged at
+ * the end.  The result is the attention of tileattn_fwd (bf16, is_f16 = 0)
+ * or tileattn_fwd_f16 (is_f16 != 0), up to the rounding order of that fold.
+ * It pays where few query tiles cover long key ranges (a small batch of
+ * heads, causal heads whose diagonal query tiles dominate, short queries
+ * against a long context): there the plain grid leaves most compute units
+ * idle while its heaviest query tiles run.
+ *   workspace       : device memory, 16-byte aligned, of at least
+ *                     tileattn_fwd_workspace_size(...) bytes for the same
+ *                     problem on the same device; owned by the caller, its
+ *                     contents on entry do not matter and on return are
+ *                     undefined.  Calls that share a workspace must be
+ *                     ordered (one stream, or synchronised).
+ *   workspace_bytes : its size in bytes.
+ * Where tileattn_fwd_workspace_size is 0 the call is tileattn_fwd /
+ * tileattn_fwd_f16 and workspace may be NULL.  Otherwise it launches two
+ * kernels on `stream`.  Extra error: TILEATTN_ERR_WORKSPACE (workspace NULL
+ * or workspace_bytes too small), TILEATTN_ERR_ALIGNMENT for a misaligned
+ * workspace.
+ */
+int tileattn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                    float scale, int causal, int is_f16, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes tileattn_fwd_ws needs for this problem on the current
+ * device (0: it needs none), or a negative tileattn_status for a bad shape.
+ * The split depends on the device's compute unit count.
+ */
+long long tileattn_fwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal);
 
 /*
  * float32 attention forward: the same contract as tileattn_fwd with fp32

@@ -17,8 +17,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtileattn.so")
 
-EXPORTED = ("tileattn_fwd", "tileattn_fwd_f16", "tileattn_fwd_ext", "tileattn_fwd_f32",
-            "tileattn_matmul", "tileattn_softmax", "tileattn_gelu", "tileattn_strerror",
+EXPORTED = ("tileattn_fwd", "tileattn_fwd_f16", "tileattn_fwd_ext", "tileattn_fwd_ws",
+            "tileattn_fwd_workspace_size", "tileattn_fwd_f32", "tileattn_matmul", "tileattn_softmax", "tileattn_gelu", "tileattn_strerror",
             "tileattn_launch_shape")
 
 DTYPE_F32, DTYPE_BF16 = 0, 1  # tileattn_dtype codes
@@ -34,6 +34,7 @@ STATUS = {
     -7: "TILEATTN_ERR_TOO_LARGE",
     -8: "TILEATTN_ERR_LAUNCH",
     -9: "TILEATTN_ERR_DTYPE",
+    -10: "TILEATTN_ERR_WORKSPACE",
 }
 
 _lib = None
@@ -63,6 +64,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tileattn_fwd_f16.restype = i
     lib.tileattn_fwd_ext.argtypes = sig[:13] + [vp, vp, i, i, vp]
     lib.tileattn_fwd_ext.restype = i
+    lib.tileattn_fwd_ws.argtypes = sig[:13] + [i, vp, ctypes.c_size_t, vp]
+    lib.tileattn_fwd_ws.restype = i
+    lib.tileattn_fwd_workspace_size.argtypes = [i] * 7
+    lib.tileattn_fwd_workspace_size.restype = ctypes.c_longlong
     lib.tileattn_fwd_f32.argtypes = sig
     lib.tileattn_fwd_f32.restype = i
     lib.tileattn_matmul.argtypes = [vp, vp, vp, i, i, i, i, vp]
@@ -97,6 +102,17 @@ def tileattn_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, alib
     return load_library().tileattn_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, float(scale),
                                            int(bool(causal)), alibi_slopes, block_mask, mask_heads,
                                            int(bool(is_f16)), stream)
+
+
+def tileattn_fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, is_f16, workspace,
+                    workspace_bytes, stream) -> int:
+    return load_library().tileattn_fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, float(scale),
+                                          int(bool(causal)), int(bool(is_f16)), workspace,
+                                          workspace_bytes, stream)
+
+
+def tileattn_fwd_workspace_size(B, Hq, Hkv, Sq, Sk, D, causal) -> int:
+    return load_library().tileattn_fwd_workspace_size(B, Hq, Hkv, Sq, Sk, D, int(bool(causal)))
 
 
 def tileattn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream) -> int:
@@ -137,7 +153,7 @@ def _overlap(a, b) -> bool:
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
-            stream=None, alibi_slopes=None, block_mask=None):
+            stream=None, alibi_slopes=None, block_mask=None, key_chunks: bool = True):
     """Attention forward on the GPU: returns (o, lse).
 
     q [B, Hq, Sq, D], k/v [B, Hkv, Sk, D]: contiguous bf16, fp16 or fp32 tensors on
@@ -148,6 +164,12 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     ``alibi_slopes`` (float32 [Hq]) and/or ``block_mask`` (uint8
     [1 or Hq, ceil(Sq/64), ceil(Sk/64)]), both on q's device, select
     ``tileattn_fwd_ext`` (bf16 or fp16 inputs only).
+
+    Plain bf16 / fp16 calls go through ``tileattn_fwd_ws`` when
+    ``key_chunks`` is true (the default): where the library splits query
+    tiles' key ranges over several workgroups, its workspace is a torch
+    allocation on the launch stream.  ``key_chunks=False`` calls
+    ``tileattn_fwd`` / ``tileattn_fwd_f16``, which never split.
     """
     import torch
 
@@ -203,7 +225,20 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     fn = tileattn_fwd_ext if ext else entry[q.dtype]
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
-        if ext:
+        ws_bytes = 0
+        if key_chunks and not ext and q.dtype != torch.float32:
+            ws_bytes = tileattn_fwd_workspace_size(B, Hq, Hkv, Sq, Sk, D, causal)
+            if ws_bytes < 0:
+                raise TileAttnError(ws_bytes, "tileattn_fwd_workspace_size")
+        if ws_bytes > 0:
+            fn = tileattn_fwd_ws
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+            if s != torch.cuda.current_stream(q.device):
+                ws.record_stream(s)
+            rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, Hq, Hkv, Sq, Sk, D, scale, causal, int(q.dtype == torch.float16),
+                    ws.data_ptr(), ws_bytes, s.cuda_stream)
+        elif ext:
             rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                     B, Hq, Hkv, Sq, Sk, D, scale, causal,
                     None if alibi_slopes is None else alibi_slopes.data_ptr(),

@@ -65,6 +65,7 @@
 //     a linear (ALiBi) bias start the score product from the bias, and walk
 //     the key tiles from the diagonal down when causal.
 
+#include <algorithm>
 #include <atomic>
 
 #include "../../include/tileattn.h"
@@ -81,6 +82,11 @@ constexpr int kBlockNF32 = 32;                         // keys per tile (fp32 pa
 
 // Capacity of the per-workgroup tile list of block-masked calls: Sk <= 64 * this.
 constexpr int kMaxMaskedTiles = 2048;
+// Chunked key split: workspace floats per chunk (one 128-row workgroup): the
+// fp32 accumulator, then the rows' reference max and running sum.
+constexpr int kChunkRows = 128;
+template <int D>
+constexpr int kChunkFloats = kChunkRows * D + 2 * kChunkRows;
 
 // ---------------------------------------------------------------------------
 // bf16 kernel
@@ -216,9 +222,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     const uint16_t* __restrict__ Q, const uint16_t* K,
     const uint16_t* V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Hq, int Hkv, int Sq, int Sk, float scale, int nqt, int nwg,
-    const float* __restrict__ slopes, const unsigned char* __restrict__ bmask, int mask_heads) {
+    const float* __restrict__ slopes, const unsigned char* __restrict__ bmask, int mask_heads,
+    int chunk_tiles, float* __restrict__ ws) {
   using T = Bf16Tile<D, SPLIT>;
   static_assert(T::kThreads == 512, "two groups of four waves");
+  static_assert(!SPLIT || T::kBlockM == kChunkRows, "a chunk is one key-split workgroup");
   __shared__ __attribute__((aligned(16)))
   unsigned char smem[T::kSmemBytes];
 
@@ -230,8 +238,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int group = wave >> 2;
   const int G = Hq / Hkv;
 
+  // Chunked key split (key-split instances with chunk_tiles > 0): the grid
+  // is chunk-major, workgroup u = c * nwg + w taking key tiles
+  // c * chunk_tiles to c * chunk_tiles + chunk_tiles - 1 of the query tile
+  // that workgroup w of the plain grid has.  chunk_tiles is even, so only a
+  // query tile's last chunk can be odd.  A chunk past the query tile's last
+  // key tile has nothing to do.
+  const bool chunked = SPLIT && chunk_tiles > 0;
+  const int chunk = chunked ? (int)blockIdx.x / nwg : 0;
   int b, hq, qt;
-  map_workgroup(blockIdx.x, nwg, Hkv, G, nqt, CAUSAL, b, hq, qt);
+  map_workgroup((int)blockIdx.x - chunk * nwg, nwg, Hkv, G, nqt, CAUSAL, b, hq, qt);
   const int hk = hq / G;
   const int q0 = qt * T::kBlockM;
   const int rw = SPLIT ? (wave & 3) : wave;  // row wave: which 32 rows of the workgroup
@@ -248,6 +264,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     const int last_row = min(q0 + T::kBlockM - 1, Sq - 1);
     nkt = min(nkt, last_row / kBlockN + 1);
   }
+  const int nchunks = chunked ? (nkt + chunk_tiles - 1) / chunk_tiles : 1;
+  if (chunk >= nchunks) return;
 
   // Key tiles the workgroup visits.  Without a block mask: tiles 0..nkt-1.
   // With one: the tiles that any of the workgroup's four 64-row query
@@ -292,8 +310,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   // end: without a mask, a tile past the keys (past Sk, or past every row's
   // diagonal), whose loads read zeros and whose scores the mask hides; with
   // one, no list entry, which no wave sees.  Either way it changes nothing.
-  const int nl = nt;
-  const int lbase = SPLIT ? group * ((nl + 1) / 2) : 0;
+  // A chunk covers tiles t0 to t0 + nl - 1; only the last chunk of a query
+  // tile can have an odd count, so only there does group 1 reach one past
+  // the end, the tile nkt past the keys, as without chunks.  (The block-mask
+  // instances take no chunks.)
+  const int t0 = chunk * chunk_tiles;
+  const int nl = chunked ? min(chunk_tiles, nkt - t0) : nt;
+  const int lbase = (chunked ? t0 : 0) + (SPLIT ? group * ((nl + 1) / 2) : 0);
   if (SPLIT) nt = (nl + 1) / 2;
   auto in_list = [&](int j) -> bool { return !SPLIT || lbase + order(j) < nl; };
   auto tile = [&](int j) -> int {
@@ -633,8 +656,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
   }
 
-  // ---- epilogue: O = acc / l, lse = m*scale + ln l = mref*ln2 + ln l ---------
+  // ---- a chunk of several: its partial state goes to the workspace --------
+  // The unnormalised acc in the accumulator's own register layout (entry
+  // ((rw * D/32 + db) * 4 + g) * 64 + lane of f32x4, i.e. 1 KiB per store
+  // instruction), then the rows' reference max (exp2 units) and sum;
+  // attn_merge_kernel combines the chunks of the query tile.  Rows past Sq
+  // are not written.
   const float l_tot = wave_pair_sum(l_run);
+  if (chunked && nchunks > 1) {
+    if (group == 0 && my_row < Sq) {
+      float* const part = ws + (size_t)blockIdx.x * kChunkFloats<D>;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(part + (((rw * (D / 32) + db) * 4 + g) * 64 + lane) * 4) =
+              f32x4{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+      if (half == 0) {
+        part[kChunkRows * D + rw * kRowsPerWave + l32] = mref;
+        part[kChunkRows * D + kChunkRows + rw * kRowsPerWave + l32] = l_tot;
+      }
+    }
+    return;
+  }
+
+  // ---- epilogue: O = acc / l, lse = m*scale + ln l = mref*ln2 + ln l ---------
   // Block mask: a row with no visible key (l = 0, mref = -FLT_MAX) gets
   // o = 0, lse = -inf.
   const float inv = (MASK && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
@@ -675,6 +721,99 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
       __builtin_amdgcn_raw_buffer_store_b128(orow[i], orsrc, (i * 64 + lane) * 16, 0, 0);
   }
   if (row_owner && half == 0 && my_row < Sq) LSE[q_head + my_row] = mref * kLn2 + logf(l_tot);
+}
+
+// ---------------------------------------------------------------------------
+// Merge of a chunked key split: per query tile with several chunks, the
+// chunks' partial states (acc, reference max m and sum l of every row, over
+// disjoint key ranges) combine as the online softmax combines two tiles:
+// with M = max_c m_c, O = sum_c 2^(m_c - M) acc_c / L, L = sum_c 2^(m_c - M) l_c,
+// lse = M ln 2 + ln L.  Workgroup 4 w + s takes rows 32 s to 32 s + 31 of
+// workgroup w's query tile; its 256 threads read the chunks' accumulators
+// in their stored order (a thread keeps one row and D / 8 of its columns),
+// and the rows leave through LDS whole.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool IS_F16>
+__global__ __launch_bounds__(256) void attn_merge_kernel(
+    const float* __restrict__ ws, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    int Hq, int Hkv, int Sq, int Sk, int nqt, int nwg, int chunk_tiles) {
+  constexpr int kPitch = D * 2 + 16;  // bytes per staged output row
+  __shared__ __attribute__((aligned(16))) unsigned char stage[kRowsPerWave * kPitch];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g = tid >> 6;
+  const int w = (int)blockIdx.x >> 2, slice = (int)blockIdx.x & 3;
+  int b, hq, qt;
+  map_workgroup(w, nwg, Hkv, Hq / Hkv, nqt, CAUSAL, b, hq, qt);
+  const int q0 = qt * kChunkRows + slice * kRowsPerWave;
+  int nkt = (Sk + kBlockN - 1) / kBlockN;
+  if (CAUSAL) nkt = min(nkt, min(qt * kChunkRows + kChunkRows - 1, Sq - 1) / kBlockN + 1);
+  const int nchunks = (nkt + chunk_tiles - 1) / chunk_tiles;
+  if (nchunks < 2 || q0 >= Sq) return;  // a single chunk wrote its own rows
+
+  const int r = slice * kRowsPerWave + (lane & 31);  // row within the query tile
+  const bool live = q0 + (lane & 31) < Sq;             // rows past Sq were not written
+  float M = -FLT_MAX, L = 0.f;
+  f32x4 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Chunks in batches of kBatch: all loads of a batch are issued before the
+  // first is used.  A chunk past the last (m = -FLT_MAX, l = 0, acc = 0)
+  // adds nothing.
+  constexpr int kBatch = 4;
+  for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+    float m[kBatch], l[kBatch];
+    f32x4 x[kBatch][D / 32];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      m[u] = -FLT_MAX;
+      l[u] = 0.f;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) x[u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (live && c0 + u < nchunks) {
+        const float* part = ws + (size_t)((c0 + u) * nwg + w) * kChunkFloats<D>;
+        m[u] = part[kChunkRows * D + r];
+        l[u] = part[kChunkRows * D + kChunkRows + r];
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+          x[u][i] = *reinterpret_cast<const f32x4*>(part + (((slice * (D / 32) + i) * 4 + g) * 64 + lane) * 4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float mn = fmaxf(M, m[u]);
+      const float a = __builtin_amdgcn_exp2f(M - mn), bw = __builtin_amdgcn_exp2f(m[u] - mn);
+      M = mn;
+      L = fmaf(L, a, l[u] * bw);
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(acc[i][e], a, x[u][i][e] * bw);
+    }
+  }
+  const float inv = 1.0f / L;
+  // Element e of acc[i] is column 32 i + 8 g + 4 (lane / 32) + e of row r.
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    __bf16 o4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o4[e] = round16<IS_F16>(acc[i][e] * inv);
+    uint2 u;
+    u.x = (uint32_t)__builtin_bit_cast(uint16_t, o4[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, o4[1]) << 16);
+    u.y = (uint32_t)__builtin_bit_cast(uint16_t, o4[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, o4[3]) << 16);
+    *reinterpret_cast<uint2*>(stage + (lane & 31) * kPitch + (32 * i + 8 * g + 4 * (lane >> 5)) * 2) = u;
+  }
+  const size_t q_head = ((size_t)b * Hq + hq) * (size_t)Sq;
+  if (tid < kRowsPerWave && q0 + tid < Sq) LSE[q_head + q0 + tid] = M * kLn2 + logf(L);
+  __syncthreads();
+  constexpr int kPieces = kRowsPerWave * D * 2 / 16;  // 16-byte pieces of the slice
+#pragma unroll
+  for (int p = tid; p < kPieces; p += 256) {
+    const int row = p / (D / 8), col = p % (D / 8);
+    if (q0 + row < Sq)
+      *reinterpret_cast<u32x4*>(O + (q_head + q0 + row) * D + col * 8) =
+          *reinterpret_cast<const u32x4*>(stage + row * kPitch + col * 16);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -859,18 +998,21 @@ int launch(Kern kernel, const TIn* q, const TIn* k, const TIn* v, TOut* o, float
   return e == hipSuccess ? TILEATTN_OK : TILEATTN_ERR_LAUNCH;
 }
 
-// The 16-bit kernel takes three more arguments (bias slopes, block mask and
-// its head count); the plain entry points pass none.
+// The 16-bit kernel takes five more arguments (bias slopes, block mask and
+// its head count, and the chunked key split's chunk length and workspace);
+// the plain entry points pass none.  With chunks the grid is chunk-major:
+// max_chunks copies of the plain grid.
 template <int BLOCK_M, int THREADS, typename Kern>
 int launch16(Kern kernel, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
              float* lse, int B, int Hq, int Hkv, int Sq, int Sk, float scale,
-             const float* slopes, const unsigned char* bmask, int mask_heads, void* stream) {
+             const float* slopes, const unsigned char* bmask, int mask_heads, void* stream,
+             int chunk_tiles = 0, int max_chunks = 1, float* ws = nullptr) {
   const int nqt = (Sq + BLOCK_M - 1) / BLOCK_M;
   const int nwg = B * Hq * nqt;
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&Hq,
                   (void*)&Hkv, (void*)&Sq, (void*)&Sk, (void*)&scale, (void*)&nqt, (void*)&nwg,
-                  (void*)&slopes, (void*)&bmask, (void*)&mask_heads};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(nwg), dim3(THREADS),
+                  (void*)&slopes, (void*)&bmask, (void*)&mask_heads, (void*)&chunk_tiles, (void*)&ws};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(nwg * max_chunks), dim3(THREADS),
                                  args, 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TILEATTN_OK : TILEATTN_ERR_LAUNCH;
 }
@@ -895,6 +1037,71 @@ int compute_units() {
 bool use_split(int B, int Hq, int Sq) {
   const long long wg256 = (long long)B * Hq * ((Sq + 255) / 256);
   return 2 * wg256 <= compute_units();
+}
+
+// Chunked key split (tileattn_fwd_ws): on a key-split grid whose heaviest
+// query tile has far more key tiles than the chip's balanced share, the
+// query tiles' key ranges are cut into chunks of about that share (an even
+// number of tiles, at least kMinChunkTiles), each its own workgroup, and a
+// second kernel merges the chunks of each query tile.  Without it the grid
+// lasts as long as its heaviest query tile while most compute units idle.
+// The merge and the partial states cost about 5 us; measured on MI355X, a
+// split pays once the heaviest query tile has 1.5 chunks and at least
+// kMinSplitTiles key tiles (at 32 tiles, a 2K causal grid, it lost 15%).
+constexpr int kMinChunkTiles = 16;
+constexpr int kMinSplitTiles = 48;
+
+struct ChunkPlan {
+  int chunk_tiles = 0;  // 0: no chunks
+  int max_chunks = 1;   // chunks of the heaviest query tile
+  size_t bytes = 0;     // workspace bytes
+};
+
+ChunkPlan chunk_plan(int B, int Hq, int Sq, int Sk, int D, bool causal) {
+  ChunkPlan plan;
+  if (B == 0 || Hq == 0 || Sq == 0 || !use_split(B, Hq, Sq)) return plan;
+  const int nqt = (Sq + kChunkRows - 1) / kChunkRows;
+  const int n = (Sk + kBlockN - 1) / kBlockN;
+  long long per_head = 0;
+  int max_nk = 0;
+  for (int qt = 0; qt < nqt; ++qt) {
+    const int nk = causal ? std::min(n, std::min(qt * kChunkRows + kChunkRows - 1, Sq - 1) / kBlockN + 1) : n;
+    per_head += nk;
+    max_nk = std::max(max_nk, nk);
+  }
+  const long long units = compute_units();
+  const long long share = ((long long)B * Hq * per_head + units - 1) / units;
+  const int c = (int)std::max<long long>(kMinChunkTiles, (share + 1) & ~1LL);
+  if (2 * max_nk < 3 * c || max_nk < kMinSplitTiles) return plan;
+  plan.chunk_tiles = c;
+  plan.max_chunks = (max_nk + c - 1) / c;
+  plan.bytes = (size_t)plan.max_chunks * B * Hq * nqt * (size_t)(kChunkRows * D + 2 * kChunkRows) * sizeof(float);
+  return plan;
+}
+
+template <int D, bool IS_F16>
+int launch_chunked(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                   int B, int Hq, int Hkv, int Sq, int Sk, float scale, int causal,
+                   const ChunkPlan& plan, float* ws, void* stream) {
+  using T = Bf16Tile<D, true>;
+  const int st = causal
+      ? launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, true, IS_F16, false, false, true>, q, k, v, o,
+                                          lse, B, Hq, Hkv, Sq, Sk, scale, nullptr, nullptr, 1, stream,
+                                          plan.chunk_tiles, plan.max_chunks, ws)
+      : launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, false, IS_F16, false, false, true>, q, k, v, o,
+                                          lse, B, Hq, Hkv, Sq, Sk, scale, nullptr, nullptr, 1, stream,
+                                          plan.chunk_tiles, plan.max_chunks, ws);
+  if (st != TILEATTN_OK) return st;
+  int nqt = (Sq + kChunkRows - 1) / kChunkRows;
+  int nwg = B * Hq * nqt;
+  int chunk_tiles = plan.chunk_tiles;
+  const float* wsc = ws;
+  void* args[] = {(void*)&wsc, (void*)&o, (void*)&lse, (void*)&Hq, (void*)&Hkv, (void*)&Sq,
+                  (void*)&Sk, (void*)&nqt, (void*)&nwg, (void*)&chunk_tiles};
+  const void* merge = causal ? reinterpret_cast<const void*>(attn_merge_kernel<D, true, IS_F16>)
+                             : reinterpret_cast<const void*>(attn_merge_kernel<D, false, IS_F16>);
+  hipError_t e = hipLaunchKernel(merge, dim3(4 * nwg), dim3(256), args, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TILEATTN_OK : TILEATTN_ERR_LAUNCH;
 }
 
 template <int D, bool IS_F16, bool MASK, bool ALIBI, bool SPLIT>
@@ -948,6 +1155,31 @@ int fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int 
 #undef TILEATTN_V16
 }
 
+// tileattn_fwd_ws: the chunked key split where chunk_plan takes it (plain
+// bf16 / fp16 only), else the plain kernel.
+int fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+           int Hkv, int Sq, int Sk, int D, float scale, int causal, int is_f16, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  bool empty;
+  const int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty);
+  if (st != TILEATTN_OK || empty) return st;
+  const ChunkPlan plan = chunk_plan(B, Hq, Sq, Sk, D, causal != 0);
+  if (plan.chunk_tiles == 0)
+    return is_f16 ? fwd16<true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, nullptr, nullptr, 1, stream)
+                  : fwd16<false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, nullptr, nullptr, 1, stream);
+  if (workspace == nullptr || workspace_bytes < plan.bytes) return TILEATTN_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return TILEATTN_ERR_ALIGNMENT;
+  auto qq = static_cast<const uint16_t*>(q), kk = static_cast<const uint16_t*>(k),
+       vv = static_cast<const uint16_t*>(v);
+  auto oo = static_cast<uint16_t*>(o);
+  auto ws = static_cast<float*>(workspace);
+  if (D == 128)
+    return is_f16 ? launch_chunked<128, true>(qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, causal, plan, ws, stream)
+                  : launch_chunked<128, false>(qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, causal, plan, ws, stream);
+  return is_f16 ? launch_chunked<64, true>(qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, causal, plan, ws, stream)
+                : launch_chunked<64, false>(qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, causal, plan, ws, stream);
+}
+
 }  // namespace
 
 extern "C" int tileattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -971,6 +1203,23 @@ extern "C" int tileattn_fwd_ext(const void* q, const void* k, const void* v, voi
                               block_mask, mask_heads, stream)
                 : fwd16<false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, alibi_slopes,
                                block_mask, mask_heads, stream);
+}
+
+extern "C" long long tileattn_fwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                                 int causal) {
+  bool empty;
+  static const float dummy[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
+  const int st = validate(dummy, dummy, dummy, dummy, dummy, B, Hq, Hkv, Sq, Sk, D, 1.0f, &empty);
+  if (st != TILEATTN_OK) return st;
+  return empty ? 0 : (long long)chunk_plan(B, Hq, Sq, Sk, D, causal != 0).bytes;
+}
+
+extern "C" int tileattn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                               int causal, int is_f16, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, is_f16, workspace,
+                workspace_bytes, stream);
 }
 
 extern "C" int tileattn_fwd_f32(const float* q, const float* k, const float* v, float* o,
@@ -998,6 +1247,7 @@ extern "C" const char* tileattn_strerror(int status) {
     case TILEATTN_ERR_TOO_LARGE: return "problem exceeds the index range";
     case TILEATTN_ERR_LAUNCH: return "kernel launch failed (is a gfx950 device current?)";
     case TILEATTN_ERR_DTYPE: return "unknown dtype code";
+    case TILEATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than tileattn_fwd_workspace_size";
     default: return "unknown tileattn status";
   }
 }
