@@ -64,7 +64,8 @@ typedef enum {
                                   /* with 32-bit buffer offsets)                      */
   TILEATTN_ERR_LAUNCH = -8,       /* the HIP launch failed (e.g. no gfx950 device)    */
   TILEATTN_ERR_DTYPE = -9,        /* unknown tileattn_dtype code                      */
-  TILEATTN_ERR_WORKSPACE = -10    /* workspace NULL or below the size it needs        */
+  TILEATTN_ERR_WORKSPACE = -10,   /* workspace NULL or below the size it needs        */
+  TILEATTN_ERR_SCRATCH = -11      /* tileattn_fwd_noalloc: over its static workspace  */
 } tileattn_status;
 
 /* Storage type codes of tileattn_softmax and tileattn_gelu. */
@@ -174,6 +175,26 @@ int tileattn_fwd_ws(const void* q, const void* k, const void* v, void* o, float*
  * The split depends on the device's compute unit count.
  */
 long long tileattn_fwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal);
+
+/*
+ * tileattn_fwd_ws without the workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It allocates nothing: the workspace is
+ * a static 64 MiB device array of the library, one per device, loaded with
+ * the library's code and held until the process ends; the first call on a
+ * device looks up its address (hipGetSymbolAddress) with that device
+ * current.  Same arguments, results and errors as tileattn_fwd_ws (bitwise
+ * the same results), plus TILEATTN_ERR_SCRATCH for a problem whose
+ * tileattn_fwd_workspace_size exceeds 64 MiB (none does on a 256-CU device:
+ * the largest split needs about 51 MB at D = 128); TILEATTN_ERR_LAUNCH if
+ * the address lookup fails.  Every call on a device shares its array and
+ * nothing in it needs clearing between calls (each call writes every part
+ * it reads), so calls that overlap on one device (different streams or
+ * host threads without ordering) race and must be serialised by the caller.
+ */
+int tileattn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                         float scale, int causal, int is_f16, void* stream);
 
 /*
  * float32 attention forward: the same contract as tileattn_fwd with fp32

@@ -3,7 +3,8 @@
 ``forward(q, k, v, causal, scale) -> (o, lse)``, ``matmul(a, b) -> c``,
 ``softmax(x) -> out`` and ``gelu(x, w, b) -> out`` are the torch-facing
 entries; ``tileattn_fwd`` / ``tileattn_fwd_f16`` / ``tileattn_fwd_ext`` /
-``tileattn_fwd_ws`` / ``tileattn_fwd_workspace_size`` / ``tileattn_fwd_f32`` / ``tileattn_matmul`` / ``tileattn_softmax`` /
+``tileattn_fwd_ws`` / ``tileattn_fwd_workspace_size`` / ``tileattn_fwd_noalloc`` /
+``tileattn_fwd_f32`` / ``tileattn_matmul`` / ``tileattn_softmax`` /
 ``tileattn_gelu`` / ``tileattn_strerror`` /
 ``tileattn_launch_shape`` mirror the C functions of ``include/tileattn.h``.
 The shared library is loaded on first use and must have been built
@@ -23,6 +24,7 @@ from .binding import (  # noqa: F401
     tileattn_fwd_ext,
     tileattn_fwd_f16,
     tileattn_fwd_f32,
+    tileattn_fwd_noalloc,
     tileattn_fwd_workspace_size,
     tileattn_fwd_ws,
     tileattn_gelu,

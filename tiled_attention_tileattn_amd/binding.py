@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtileattn.so")
 
 EXPORTED = ("tileattn_fwd", "tileattn_fwd_f16", "tileattn_fwd_ext", "tileattn_fwd_ws",
-            "tileattn_fwd_workspace_size", "tileattn_fwd_f32", "tileattn_matmul", "tileattn_softmax", "tileattn_gelu", "tileattn_strerror",
+            "tileattn_fwd_workspace_size", "tileattn_fwd_noalloc", "tileattn_fwd_f32", "tileattn_matmul", "tileattn_softmax", "tileattn_gelu", "tileattn_strerror",
             "tileattn_launch_shape")
 
 DTYPE_F32, DTYPE_BF16 = 0, 1  # tileattn_dtype codes
@@ -35,6 +35,7 @@ STATUS = {
     -8: "TILEATTN_ERR_LAUNCH",
     -9: "TILEATTN_ERR_DTYPE",
     -10: "TILEATTN_ERR_WORKSPACE",
+    -11: "TILEATTN_ERR_SCRATCH",
 }
 
 _lib = None
@@ -68,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tileattn_fwd_ws.restype = i
     lib.tileattn_fwd_workspace_size.argtypes = [i] * 7
     lib.tileattn_fwd_workspace_size.restype = ctypes.c_longlong
+    lib.tileattn_fwd_noalloc.argtypes = sig[:13] + [i, vp]
+    lib.tileattn_fwd_noalloc.restype = i
     lib.tileattn_fwd_f32.argtypes = sig
     lib.tileattn_fwd_f32.restype = i
     lib.tileattn_matmul.argtypes = [vp, vp, vp, i, i, i, i, vp]
@@ -113,6 +116,11 @@ def tileattn_fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, is_f1
 
 def tileattn_fwd_workspace_size(B, Hq, Hkv, Sq, Sk, D, causal) -> int:
     return load_library().tileattn_fwd_workspace_size(B, Hq, Hkv, Sq, Sk, D, int(bool(causal)))
+
+
+def tileattn_fwd_noalloc(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, is_f16, stream) -> int:
+    return load_library().tileattn_fwd_noalloc(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, float(scale),
+                                               int(bool(causal)), int(bool(is_f16)), stream)
 
 
 def tileattn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream) -> int:

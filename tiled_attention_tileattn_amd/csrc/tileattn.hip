@@ -67,6 +67,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "../../include/tileattn.h"
 #include "attn_common.h"
@@ -1182,6 +1183,39 @@ int fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse, int
 
 }  // namespace
 
+// Workspace of tileattn_fwd_noalloc: one array per device, loaded with the
+// code object and held until the process ends.  Host code never passes its
+// name to a kernel (on the host it is a stand-in, not a device address);
+// scratch_address() looks up the device address once per device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+
+// Device address of `scratch` on the current device, or nullptr if the
+// lookup fails.  The first call on a device looks it up with that device
+// current and keeps it.
+float* scratch_address() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<float*> addr[kMaxDevices];
+  static std::mutex lookup;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  float* p = addr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> guard(lookup);
+  p = addr[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || a == nullptr) return nullptr;
+    p = static_cast<float*>(a);
+    addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
 extern "C" int tileattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
                             int causal, void* stream) {
@@ -1222,6 +1256,21 @@ extern "C" int tileattn_fwd_ws(const void* q, const void* k, const void* v, void
                 workspace_bytes, stream);
 }
 
+extern "C" int tileattn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                                    int causal, int is_f16, void* stream) {
+  bool empty;
+  const int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty);
+  if (st != TILEATTN_OK || empty) return st;
+  const ChunkPlan plan = chunk_plan(B, Hq, Sq, Sk, D, causal != 0);
+  if (plan.chunk_tiles == 0)  // no chunks: the plain kernel, no workspace
+    return fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, is_f16, nullptr, 0, stream);
+  if (plan.bytes > kScratchBytes) return TILEATTN_ERR_SCRATCH;
+  float* const ws = scratch_address();
+  if (ws == nullptr) return TILEATTN_ERR_LAUNCH;
+  return fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, is_f16, ws, kScratchBytes, stream);
+}
+
 extern "C" int tileattn_fwd_f32(const float* q, const float* k, const float* v, float* o,
                                 float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int D,
                                 float scale, int causal, void* stream) {
@@ -1248,6 +1297,7 @@ extern "C" const char* tileattn_strerror(int status) {
     case TILEATTN_ERR_LAUNCH: return "kernel launch failed (is a gfx950 device current?)";
     case TILEATTN_ERR_DTYPE: return "unknown dtype code";
     case TILEATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than tileattn_fwd_workspace_size";
+    case TILEATTN_ERR_SCRATCH: return "problem needs more than the 64 MiB static workspace of tileattn_fwd_noalloc";
     default: return "unknown tileattn status";
   }
 }
