@@ -268,9 +268,13 @@ const char* tileattn_strerror(int status);
  * device's compute-unit count (queried once per device; 256 when no device
  * answers).  dtype_bytes is 2 (bf16 or fp16: the plain entry points, which
  * use 256-row workgroups, or the key split's 128-row ones when the 256-row
- * grid would fill at most half of the compute units; tileattn_fwd_ext with
- * a bias or a block mask always uses 256) or 4
- * (fp32).  Returns TILEATTN_OK or the error tileattn_fwd would.
+ * grid would fill at most half of the compute units) or 4 (fp32).  A 16-bit
+ * workgroup's rows are P query heads that share a KV head times
+ * block_m / P consecutive positions, P the largest power of two dividing
+ * Hq / Hkv and at most block_m / 32; the workgroup count is
+ * B * (Hq / P) * ceil(Sq / (block_m / P)).  (tileattn_fwd_ext with a block
+ * mask takes P at most block_m / 64.)  Returns TILEATTN_OK or the error
+ * tileattn_fwd would.
  */
 int tileattn_launch_shape(int dtype_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D,
                           int causal, int* block_m, int* block_n, long long* workgroups);

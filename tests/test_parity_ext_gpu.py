@@ -143,3 +143,14 @@ def test_ext_steep_slopes(causal):
     # slopes up to 4 per key: the weight sits on the few keys next to the row
     _run(1, 4, 2, 333, 333, 128, causal, "bf16", seed=95, use_slopes=[4.0, 1.0, 0.25, 0.0],
          mask_heads=0)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_ext_packed_heads_256_rows(kind):
+    # 8 query heads per KV head on 256-row workgroups: with a block mask the
+    # workgroup packs 4 heads x 64 positions (each 64-position query block
+    # whole), without one (bias only) 8 heads x 32 positions; every wave
+    # takes its own head's slope and mask plane.
+    use_slopes, mh = kind
+    mh = 64 if mh == "Hq" else mh
+    _run(2, 64, 8, 600, 600, 64, True, "bf16", seed=96, use_slopes=use_slopes, mask_heads=mh)

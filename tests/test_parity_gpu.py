@@ -182,7 +182,9 @@ def test_causal_row_zero_is_first_value_row():
     assert torch.equal(o.cpu()[:, :, 0], v.repeat_interleave(2, dim=1)[:, :, 0])
 
 
-# Shapes that exercise each branch of the workgroup -> (batch, head, tile) map:
+# Shapes that exercise each branch of the workgroup -> (batch, head group,
+# query tile) map (head groups: the query heads of a KV head one workgroup
+# packs):
 # whole (batch, kv head) slots per XCD (slots a multiple of 8), slots spread
 # over XCDs by query-tile residue (1, 2 or 4 slots), and the uneven fallback.
 MAP_CASES = [
@@ -191,7 +193,7 @@ MAP_CASES = [
     (2, 4, 2, 1024, 128, True),     # 4 slots, 4 query tiles: residue split over 2 XCDs
     (1, 4, 2, 2048, 64, False),     # 2 slots, 8 query tiles: residue split over 4 XCDs
     (8, 2, 2, 512, 64, True),       # 16 slots: 2 whole slots per XCD
-    (1, 8, 2, 1030, 64, True),      # 2 slots, 5 query tiles: uneven, fallback order
+    (1, 8, 2, 1030, 64, True),      # 2 slots, 33 query tiles (4 heads x 32): fallback order
     (3, 4, 1, 600, 64, False),      # 3 slots: fallback order
 ]
 
@@ -231,8 +233,9 @@ def test_small_grids_take_128_row_workgroups():
 
 
 def test_eight_wave_residue_map_on_sampled_rows():
-    # One (batch, kv head) slot and 24 query tiles of 256 rows: the 8-wave
-    # kernel's residue split over the XCDs (192 workgroups).
+    # One (batch, kv head) slot and 192 query tiles of 8 heads x 32
+    # positions: the 8-wave kernel's residue split over the XCDs (192
+    # workgroups).
     B, Hq, Hkv, S, D = 1, 8, 1, 6144, 128
     assert ta.tileattn_launch_shape(2, B, Hq, Hkv, S, S, D, 1)[1] == 256
     q, k, v = random_qkv(B, Hq, Hkv, S, S, D, dtype="bf16", seed=20)
@@ -248,7 +251,16 @@ def test_eight_wave_residue_map_on_sampled_rows():
 
 
 def test_gqa_equals_mha_with_repeated_kv_bitwise():
-    q, k, v = random_qkv(1, 8, 2, 300, 300, 128, dtype="bf16", seed=15)
+    # Both grids take 256-row workgroups (GQA: 4 heads x 64 positions each;
+    # MHA: 256 positions of one head).  There every row visits key tiles
+    # 0, 1, ... in order, and the tiles past its diagonal that a larger
+    # workgroup adds contribute exact zeros, so the rows agree bit for bit.
+    # (The key split divides each workgroup's tiles between its two wave
+    # groups, at a point that depends on the workgroup's extent, so there the
+    # two layouts agree only up to rounding.)
+    q, k, v = random_qkv(1, 64, 16, 600, 600, 128, dtype="bf16", seed=15)
+    assert ta.tileattn_launch_shape(2, 1, 64, 16, 600, 600, 128, 1)[1] == 256
+    assert ta.tileattn_launch_shape(2, 1, 64, 64, 600, 600, 128, 1)[1] == 256
     o1, l1 = _gpu_forward(q, k, v, True, 0.0883883461356163)
     o2, l2 = _gpu_forward(q, k.repeat_interleave(4, 1).contiguous(),
                           v.repeat_interleave(4, 1).contiguous(), True, 0.0883883461356163)
@@ -371,6 +383,26 @@ def test_million_keys_few_queries():
     _parity(1, 2, 1, 3, (1 << 20) + 37, 128, False, "bf16", seed=19)
 
 
+# Head packing: a workgroup holds the largest power of two (up to 8 on 256
+# rows, 4 on 128) of the query heads sharing a KV head, each on a slice of
+# positions: G = 16, 8 and 6 (2 heads), 3 (none); decode-like rows.
+PACK_CASES = [
+    # B, Hq, Hkv, Sq, Sk, D, causal, dtype
+    (1, 16, 1, 300, 300, 128, True, "bf16"),    # key split, 4 heads x 32 positions
+    (2, 64, 8, 600, 600, 128, True, "bf16"),    # 256 rows: 8 heads x 32 positions
+    (2, 48, 8, 520, 700, 64, True, "fp16"),     # 256 rows: 2 heads x 128 positions
+    (1, 24, 8, 100, 100, 128, False, "bf16"),   # G = 3: one head per workgroup
+    (1, 32, 8, 1, 2000, 128, False, "bf16"),    # one row per head, 4 heads a workgroup
+    (4, 32, 8, 3, 700, 64, True, "fp16"),       # three rows per head, causal
+]
+
+
+@pytest.mark.parametrize("case", PACK_CASES)
+def test_head_packing(case):
+    B, Hq, Hkv, Sq, Sk, D, causal, dtype = case
+    _parity(B, Hq, Hkv, Sq, Sk, D, causal, dtype, seed=Hq + Sq + Sk)
+
+
 # Grids on either side of the workgroup-size switch (at most 128 workgroups
 # of 256 rows on a 256-CU device take 128-row workgroups instead).
 SWITCH_CASES = [
@@ -385,7 +417,10 @@ SWITCH_CASES = [
 @pytest.mark.parametrize("case", SWITCH_CASES)
 def test_workgroup_size_switch(case):
     B, Hq, Hkv, Sq, Sk, D, causal, dtype = case
-    wg256 = B * Hq * -(-Sq // 256)
+    G, p = Hq // Hkv, 1
+    while 2 * p <= 8 and G % (2 * p) == 0:
+        p *= 2
+    wg256 = B * (Hq // p) * -(-Sq // (256 // p))   # 256-row workgroups, p heads packed
     expect = 128 if 2 * wg256 <= torch.cuda.get_device_properties(0).multi_processor_count else 256
     assert ta.tileattn_launch_shape(2, B, Hq, Hkv, Sq, Sk, D, int(causal))[1] == expect
     _parity(B, Hq, Hkv, Sq, Sk, D, causal, dtype, seed=wg256 + Sq)

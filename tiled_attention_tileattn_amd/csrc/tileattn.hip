@@ -106,6 +106,7 @@ struct Bf16Tile {
   static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kRowWaves = SPLIT ? kWaves / 2 : kWaves;  // waves with distinct query rows
+  static constexpr int kRowWavesShift = SPLIT ? 2 : 3;            // log2 kRowWaves
   static constexpr int kBlockM = kRowWaves * kRowsPerWave;      // query rows per workgroup
   static constexpr int kSets = SPLIT ? 2 : 1;                    // K/V slot pairs (one per group)
   static constexpr int kChunks = D / 8;                    // 16-byte chunks per K/V row
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     const uint16_t* V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Hq, int Hkv, int Sq, int Sk, float scale, int nqt, int nwg,
     const float* __restrict__ slopes, const unsigned char* __restrict__ bmask, int mask_heads,
-    int chunk_tiles, float* __restrict__ ws) {
+    int chunk_tiles, float* __restrict__ ws, int pack_shift) {
   using T = Bf16Tile<D, SPLIT>;
   static_assert(T::kThreads == 512, "two groups of four waves");
   static_assert(!SPLIT || T::kBlockM == kChunkRows, "a chunk is one key-split workgroup");
@@ -247,12 +248,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   // key tile has nothing to do.
   const bool chunked = SPLIT && chunk_tiles > 0;
   const int chunk = chunked ? (int)blockIdx.x / nwg : 0;
-  int b, hq, qt;
-  map_workgroup((int)blockIdx.x - chunk * nwg, nwg, Hkv, G, nqt, CAUSAL, b, hq, qt);
-  const int hk = hq / G;
-  const int q0 = qt * T::kBlockM;
+  // Head packing: the workgroup's rows are 2^pack_shift consecutive query
+  // heads of one KV head (they share its K and V tiles) times PW = kBlockM /
+  // 2^pack_shift consecutive positions (a query tile).  Row wave rw takes
+  // head rw >> wph_shift of the group and positions (rw & (2^wph_shift - 1))
+  // * 32 ... + 31 of the tile.  The grid map works on head groups.
+  const int wph_shift = T::kRowWavesShift - pack_shift;  // log2 row waves per head
+  const int PW = T::kBlockM >> pack_shift;
+  int b, hgrp, qt;
+  map_workgroup((int)blockIdx.x - chunk * nwg, nwg, Hkv, G >> pack_shift, nqt, CAUSAL, b, hgrp, qt);
+  const int hq0 = hgrp << pack_shift;  // first query head of the group
+  const int hk = hq0 / G;
+  const int q0 = qt * PW;
   const int rw = SPLIT ? (wave & 3) : wave;  // row wave: which 32 rows of the workgroup
-  const int qw = q0 + rw * kRowsPerWave;
+  const int hq = hq0 + (rw >> wph_shift);    // the wave's query head
+  const int qw = q0 + ((rw & ((1 << wph_shift) - 1)) << 5);
   const int my_row = qw + l32;
 
   const size_t q_head = ((size_t)b * Hq + hq) * (size_t)Sq;
@@ -262,32 +272,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
 
   int nkt = (Sk + kBlockN - 1) / kBlockN;
   if (CAUSAL) {
-    const int last_row = min(q0 + T::kBlockM - 1, Sq - 1);
+    const int last_row = min(q0 + PW - 1, Sq - 1);
     nkt = min(nkt, last_row / kBlockN + 1);
   }
   const int nchunks = chunked ? (nkt + chunk_tiles - 1) / chunk_tiles : 1;
   if (chunk >= nchunks) return;
 
   // Key tiles the workgroup visits.  Without a block mask: tiles 0..nkt-1.
-  // With one: the tiles that any of the workgroup's four 64-row query
-  // blocks may see, in order, compacted into an LDS list by wave 0; entry =
-  // tile index (bits 0-11) | visibility of query block i (bit 12 + i).
+  // With one: the tiles that any of the workgroup's 64-row query blocks
+  // (kBlockM / 64 of them: (head, 64 positions) pairs, two row waves each;
+  // block i = row waves 2i and 2i+1) may see, in order, compacted into an
+  // LDS list by wave 0; entry = tile index (bits 0-11) | visibility of
+  // query block i (bit 12 + i).  Packing keeps PW >= 64 with a mask.
   __shared__ unsigned short tlist[MASK ? kMaxMaskedTiles : 1];
   __shared__ int tcount;
   int nt = nkt;
   if (MASK) {
     if (wave == 0) {
       const int nqb = (Sq + kBlockN - 1) / kBlockN, nkb = (Sk + kBlockN - 1) / kBlockN;
-      const unsigned char* plane = bmask + (size_t)(mask_heads == Hq ? hq : 0) * nqb * nkb;
       const int qb0 = q0 / kBlockN;
+      const int nb_shift = wph_shift - 1;  // log2 query blocks per head
       int count = 0;
       for (int base = 0; base < nkt; base += 64) {
         const int kb = base + lane;
         unsigned bits = 0;
         if (kb < nkt) {
 #pragma unroll
-          for (int i = 0; i < T::kBlockM / kBlockN; ++i)
-            if (qb0 + i < nqb && plane[(size_t)(qb0 + i) * nkb + kb] != 0) bits |= 1u << i;
+          for (int i = 0; i < T::kBlockM / kBlockN; ++i) {
+            const int qb = qb0 + (i & ((1 << nb_shift) - 1));
+            const unsigned char* plane = bmask + (size_t)(mask_heads == Hq ? hq0 + (i >> nb_shift) : 0) * nqb * nkb;
+            if (qb < nqb && plane[(size_t)qb * nkb + kb] != 0) bits |= 1u << i;
+          }
         }
         const unsigned long long vis = __ballot(bits != 0);
         const int pos = count + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(vis >> 32),
@@ -729,26 +744,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
 // chunks' partial states (acc, reference max m and sum l of every row, over
 // disjoint key ranges) combine as the online softmax combines two tiles:
 // with M = max_c m_c, O = sum_c 2^(m_c - M) acc_c / L, L = sum_c 2^(m_c - M) l_c,
-// lse = M ln 2 + ln L.  Workgroup 4 w + s takes rows 32 s to 32 s + 31 of
-// workgroup w's query tile; its 256 threads read the chunks' accumulators
-// in their stored order (a thread keeps one row and D / 8 of its columns),
-// and the rows leave through LDS whole.
+// lse = M ln 2 + ln L.  Workgroup 4 w + s takes row wave s of workgroup w
+// (32 positions of one query head, as the attention kernel's head packing
+// assigns them); its 256 threads read the chunks' accumulators in their
+// stored order (a thread keeps one row and D / 8 of its columns), and the
+// rows leave through LDS whole.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool IS_F16>
 __global__ __launch_bounds__(256) void attn_merge_kernel(
     const float* __restrict__ ws, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int Hq, int Hkv, int Sq, int Sk, int nqt, int nwg, int chunk_tiles) {
+    int Hq, int Hkv, int Sq, int Sk, int nqt, int nwg, int chunk_tiles, int pack_shift) {
   constexpr int kPitch = D * 2 + 16;  // bytes per staged output row
   __shared__ __attribute__((aligned(16))) unsigned char stage[kRowsPerWave * kPitch];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int g = tid >> 6;
   const int w = (int)blockIdx.x >> 2, slice = (int)blockIdx.x & 3;
-  int b, hq, qt;
-  map_workgroup(w, nwg, Hkv, Hq / Hkv, nqt, CAUSAL, b, hq, qt);
-  const int q0 = qt * kChunkRows + slice * kRowsPerWave;
+  const int wph_shift = 2 - pack_shift;  // log2 row waves per head (4 row waves)
+  const int PW = kChunkRows >> pack_shift;
+  int b, hgrp, qt;
+  map_workgroup(w, nwg, Hkv, (Hq / Hkv) >> pack_shift, nqt, CAUSAL, b, hgrp, qt);
+  const int hq = (hgrp << pack_shift) + (slice >> wph_shift);
+  const int q0 = qt * PW + ((slice & ((1 << wph_shift) - 1)) << 5);
   int nkt = (Sk + kBlockN - 1) / kBlockN;
-  if (CAUSAL) nkt = min(nkt, min(qt * kChunkRows + kChunkRows - 1, Sq - 1) / kBlockN + 1);
+  if (CAUSAL) nkt = min(nkt, min(qt * PW + PW - 1, Sq - 1) / kBlockN + 1);
   const int nchunks = (nkt + chunk_tiles - 1) / chunk_tiles;
   if (nchunks < 2 || q0 >= Sq) return;  // a single chunk wrote its own rows
 
@@ -1003,16 +1022,36 @@ int launch(Kern kernel, const TIn* q, const TIn* k, const TIn* v, TOut* o, float
 // its head count, and the chunked key split's chunk length and workspace);
 // the plain entry points pass none.  With chunks the grid is chunk-major:
 // max_chunks copies of the plain grid.
+// Head packing (see the kernel): log2 of the query heads one workgroup of
+// `row_waves` row waves holds: the largest power of two that divides G, at
+// most row_waves, and with a block mask at most row_waves / 2 (so that every
+// 64-position query block of the mask lies within one workgroup).
+int pack_shift_for(int G, int row_waves, bool mask) {
+  const int cap = mask ? row_waves / 2 : row_waves;
+  int s = 0;
+  while ((2 << s) <= cap && G % (2 << s) == 0) ++s;
+  return s;
+}
+
+// Workgroups of a grid of `rows`-row workgroups with head packing ps:
+// B * (Hq / 2^ps) head groups times ceil(Sq / (rows / 2^ps)) query tiles.
+long long grid_workgroups(int B, int Hq, int Sq, int rows, int ps) {
+  const int pw = rows >> ps;
+  return (long long)B * (Hq >> ps) * ((Sq + pw - 1) / pw);
+}
+
 template <int BLOCK_M, int THREADS, typename Kern>
 int launch16(Kern kernel, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
              float* lse, int B, int Hq, int Hkv, int Sq, int Sk, float scale,
-             const float* slopes, const unsigned char* bmask, int mask_heads, void* stream,
+             const float* slopes, const unsigned char* bmask, int mask_heads, int pack_shift, void* stream,
              int chunk_tiles = 0, int max_chunks = 1, float* ws = nullptr) {
-  const int nqt = (Sq + BLOCK_M - 1) / BLOCK_M;
-  const int nwg = B * Hq * nqt;
+  const int pw = BLOCK_M >> pack_shift;
+  const int nqt = (Sq + pw - 1) / pw;
+  const int nwg = B * (Hq >> pack_shift) * nqt;
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&Hq,
                   (void*)&Hkv, (void*)&Sq, (void*)&Sk, (void*)&scale, (void*)&nqt, (void*)&nwg,
-                  (void*)&slopes, (void*)&bmask, (void*)&mask_heads, (void*)&chunk_tiles, (void*)&ws};
+                  (void*)&slopes, (void*)&bmask, (void*)&mask_heads, (void*)&chunk_tiles, (void*)&ws,
+                  (void*)&pack_shift};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(nwg * max_chunks), dim3(THREADS),
                                  args, 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TILEATTN_OK : TILEATTN_ERR_LAUNCH;
@@ -1032,11 +1071,11 @@ int compute_units() {
   return n;
 }
 
-// The plain 16-bit kernel runs 256-row workgroups unless that grid would
-// leave at least half the compute units idle; then the key split's 128-row
-// workgroups, twice as many, each wave with half the tiles.
-bool use_split(int B, int Hq, int Sq) {
-  const long long wg256 = (long long)B * Hq * ((Sq + 255) / 256);
+// The 16-bit kernel runs 256-row workgroups unless that grid would leave at
+// least half the compute units idle; then the key split's 128-row
+// workgroups, each wave with half the tiles.
+bool use_split(int B, int Hq, int Hkv, int Sq, bool mask) {
+  const long long wg256 = grid_workgroups(B, Hq, Sq, 256, pack_shift_for(Hq / Hkv, 8, mask));
   return 2 * wg256 <= compute_units();
 }
 
@@ -1055,28 +1094,33 @@ constexpr int kMinSplitTiles = 48;
 struct ChunkPlan {
   int chunk_tiles = 0;  // 0: no chunks
   int max_chunks = 1;   // chunks of the heaviest query tile
+  int pack_shift = 0;   // head packing of the key-split grid
   size_t bytes = 0;     // workspace bytes
 };
 
-ChunkPlan chunk_plan(int B, int Hq, int Sq, int Sk, int D, bool causal) {
+ChunkPlan chunk_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, bool causal) {
   ChunkPlan plan;
-  if (B == 0 || Hq == 0 || Sq == 0 || !use_split(B, Hq, Sq)) return plan;
-  const int nqt = (Sq + kChunkRows - 1) / kChunkRows;
+  if (B == 0 || Hq == 0 || Sq == 0 || !use_split(B, Hq, Hkv, Sq, false)) return plan;
+  const int ps = pack_shift_for(Hq / Hkv, 4, false);
+  const int pw = kChunkRows >> ps;
+  const int nqt = (Sq + pw - 1) / pw;
   const int n = (Sk + kBlockN - 1) / kBlockN;
-  long long per_head = 0;
+  long long per_group = 0;
   int max_nk = 0;
   for (int qt = 0; qt < nqt; ++qt) {
-    const int nk = causal ? std::min(n, std::min(qt * kChunkRows + kChunkRows - 1, Sq - 1) / kBlockN + 1) : n;
-    per_head += nk;
+    const int nk = causal ? std::min(n, std::min(qt * pw + pw - 1, Sq - 1) / kBlockN + 1) : n;
+    per_group += nk;
     max_nk = std::max(max_nk, nk);
   }
+  const long long nwg = (long long)B * (Hq >> ps) * nqt;
   const long long units = compute_units();
-  const long long share = ((long long)B * Hq * per_head + units - 1) / units;
+  const long long share = (nwg / nqt * per_group + units - 1) / units;
   const int c = (int)std::max<long long>(kMinChunkTiles, (share + 1) & ~1LL);
   if (2 * max_nk < 3 * c || max_nk < kMinSplitTiles) return plan;
   plan.chunk_tiles = c;
   plan.max_chunks = (max_nk + c - 1) / c;
-  plan.bytes = (size_t)plan.max_chunks * B * Hq * nqt * (size_t)(kChunkRows * D + 2 * kChunkRows) * sizeof(float);
+  plan.pack_shift = ps;
+  plan.bytes = (size_t)plan.max_chunks * nwg * (size_t)(kChunkRows * D + 2 * kChunkRows) * sizeof(float);
   return plan;
 }
 
@@ -1087,18 +1131,20 @@ int launch_chunked(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint
   using T = Bf16Tile<D, true>;
   const int st = causal
       ? launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, true, IS_F16, false, false, true>, q, k, v, o,
-                                          lse, B, Hq, Hkv, Sq, Sk, scale, nullptr, nullptr, 1, stream,
-                                          plan.chunk_tiles, plan.max_chunks, ws)
+                                          lse, B, Hq, Hkv, Sq, Sk, scale, nullptr, nullptr, 1, plan.pack_shift,
+                                          stream, plan.chunk_tiles, plan.max_chunks, ws)
       : launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, false, IS_F16, false, false, true>, q, k, v, o,
-                                          lse, B, Hq, Hkv, Sq, Sk, scale, nullptr, nullptr, 1, stream,
-                                          plan.chunk_tiles, plan.max_chunks, ws);
+                                          lse, B, Hq, Hkv, Sq, Sk, scale, nullptr, nullptr, 1, plan.pack_shift,
+                                          stream, plan.chunk_tiles, plan.max_chunks, ws);
   if (st != TILEATTN_OK) return st;
-  int nqt = (Sq + kChunkRows - 1) / kChunkRows;
-  int nwg = B * Hq * nqt;
+  int pack_shift = plan.pack_shift;
+  const int pw = kChunkRows >> pack_shift;
+  int nqt = (Sq + pw - 1) / pw;
+  int nwg = B * (Hq >> pack_shift) * nqt;
   int chunk_tiles = plan.chunk_tiles;
   const float* wsc = ws;
   void* args[] = {(void*)&wsc, (void*)&o, (void*)&lse, (void*)&Hq, (void*)&Hkv, (void*)&Sq,
-                  (void*)&Sk, (void*)&nqt, (void*)&nwg, (void*)&chunk_tiles};
+                  (void*)&Sk, (void*)&nqt, (void*)&nwg, (void*)&chunk_tiles, (void*)&pack_shift};
   const void* merge = causal ? reinterpret_cast<const void*>(attn_merge_kernel<D, true, IS_F16>)
                              : reinterpret_cast<const void*>(attn_merge_kernel<D, false, IS_F16>);
   hipError_t e = hipLaunchKernel(merge, dim3(4 * nwg), dim3(256), args, 0, static_cast<hipStream_t>(stream));
@@ -1110,12 +1156,13 @@ int launch_waves(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16
                  int B, int Hq, int Hkv, int Sq, int Sk, float scale, int causal,
                  const float* slopes, const unsigned char* bmask, int mask_heads, void* stream) {
   using T = Bf16Tile<D, SPLIT>;
+  const int ps = pack_shift_for(Hq / Hkv, T::kRowWaves, MASK);
   return causal ? launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, true, IS_F16, MASK, ALIBI, SPLIT>,
                                                     q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, slopes, bmask,
-                                                    mask_heads, stream)
+                                                    mask_heads, ps, stream)
                 : launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, false, IS_F16, MASK, ALIBI, SPLIT>,
                                                     q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, slopes, bmask,
-                                                    mask_heads, stream);
+                                                    mask_heads, ps, stream);
 }
 
 // bf16 and fp16 inputs share one kernel template (IS_F16); a block mask and
@@ -1125,7 +1172,7 @@ int launch_variant(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint
                    int B, int Hq, int Hkv, int Sq, int Sk, float scale, int causal,
                    const float* slopes, const unsigned char* bmask, int mask_heads, void* stream) {
   // Small grids take the key split.
-  if (use_split(B, Hq, Sq))
+  if (use_split(B, Hq, Hkv, Sq, MASK))
     return launch_waves<D, IS_F16, MASK, ALIBI, true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, causal,
                                                       slopes, bmask, mask_heads, stream);
   return launch_waves<D, IS_F16, MASK, ALIBI, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, causal,
@@ -1164,7 +1211,7 @@ int fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse, int
   bool empty;
   const int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty);
   if (st != TILEATTN_OK || empty) return st;
-  const ChunkPlan plan = chunk_plan(B, Hq, Sq, Sk, D, causal != 0);
+  const ChunkPlan plan = chunk_plan(B, Hq, Hkv, Sq, Sk, D, causal != 0);
   if (plan.chunk_tiles == 0)
     return is_f16 ? fwd16<true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, nullptr, nullptr, 1, stream)
                   : fwd16<false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, nullptr, nullptr, 1, stream);
@@ -1245,7 +1292,7 @@ extern "C" long long tileattn_fwd_workspace_size(int B, int Hq, int Hkv, int Sq,
   static const float dummy[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
   const int st = validate(dummy, dummy, dummy, dummy, dummy, B, Hq, Hkv, Sq, Sk, D, 1.0f, &empty);
   if (st != TILEATTN_OK) return st;
-  return empty ? 0 : (long long)chunk_plan(B, Hq, Sq, Sk, D, causal != 0).bytes;
+  return empty ? 0 : (long long)chunk_plan(B, Hq, Hkv, Sq, Sk, D, causal != 0).bytes;
 }
 
 extern "C" int tileattn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -1262,7 +1309,7 @@ extern "C" int tileattn_fwd_noalloc(const void* q, const void* k, const void* v,
   bool empty;
   const int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty);
   if (st != TILEATTN_OK || empty) return st;
-  const ChunkPlan plan = chunk_plan(B, Hq, Sq, Sk, D, causal != 0);
+  const ChunkPlan plan = chunk_plan(B, Hq, Hkv, Sq, Sk, D, causal != 0);
   if (plan.chunk_tiles == 0)  // no chunks: the plain kernel, no workspace
     return fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, is_f16, nullptr, 0, stream);
   if (plan.bytes > kScratchBytes) return TILEATTN_ERR_SCRATCH;
@@ -1312,13 +1359,14 @@ extern "C" int tileattn_launch_shape(int dtype_bytes, int B, int Hq, int Hkv, in
   static const float dummy[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
   const int st = validate(dummy, dummy, dummy, dummy, dummy, B, Hq, Hkv, Sq, Sk, D, 1.0f, &empty);
   if (st != TILEATTN_OK) return st;
-  // 16-bit: the plain entry points' choice (the ext entry point always
-  // uses 256-row workgroups).
-  const int bm = dtype_bytes == 2 ? (use_split(B, Hq, Sq) ? Bf16Tile<128, true>::kBlockM : Bf16Tile<128>::kBlockM)
-                                  : kF32BlockM;
+  // 16-bit: the plain entry points' choice, rows = query heads x positions
+  // (head packing) per workgroup.
+  const bool split = dtype_bytes == 2 && use_split(B, Hq, Hkv, Sq, false);
+  const int bm = dtype_bytes == 2 ? (split ? Bf16Tile<128, true>::kBlockM : Bf16Tile<128>::kBlockM) : kF32BlockM;
+  const int ps = dtype_bytes == 2 ? pack_shift_for(Hq / Hkv, split ? 4 : 8, false) : 0;
   if (block_m) *block_m = bm;
   // 16-bit: 64-key tiles.
   if (block_n) *block_n = dtype_bytes == 2 ? kBlockN : kBlockNF32;
-  if (workgroups) *workgroups = empty ? 0 : (long long)B * Hq * ((Sq + bm - 1) / bm);
+  if (workgroups) *workgroups = empty ? 0 : grid_workgroups(B, Hq, Sq, bm, ps);
   return TILEATTN_OK;
 }
