@@ -18,8 +18,10 @@ rocprofv3 counter summary in profiles/ (null when the kernel changed since).
 
 ``--all`` also times, on stderr, the bf16 matrix product (tileattn_matmul),
 the row softmax and fused GELU (GB/s against the 8 TB/s HBM peak), the other
-attention workloads and the biased / block-masked variants; ``--only matmul``
-or ``--only rowwise`` times just those and prints no JSON line.
+attention workloads, the biased / block-masked variants and one KV head's
+share of the headline; ``--only matmul``, ``--only rowwise`` or ``--only
+shard`` (that share, chunked key split) times just those and prints no JSON
+line.
 """
 
 from __future__ import annotations
@@ -94,6 +96,25 @@ def time_workload(ta, w, steps, warmup, key_chunks=False):
     ev = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     del q, k, v, o, lse
     return wall_ms, float(ev.mean()), float(np.median(ev)), float(ev.min())
+
+
+def shard_lines(ta, steps, warmup, plain):
+    """One GPU's share of the headline if its KV heads were spread over Hkv
+    GPUs (head sharding needs no communication): the same call on one KV
+    head and its query heads, through tileattn_fwd (if ``plain``) and
+    through tileattn_fwd_ws (the chunked key split)."""
+    from dataclasses import replace
+
+    from tiled_attention_tileattn_amd.inputs import HEADLINE, WORKLOADS
+
+    w = WORKLOADS[HEADLINE]
+    sh = replace(w, name=f"{HEADLINE} head shard", Hq=w.Hq // w.Hkv, Hkv=1)
+    for chunks in ((False, True) if plain else (True,)):
+        _, _, med, mn = time_workload(ta, sh, steps, warmup, key_chunks=chunks)
+        entry = "tileattn_fwd_ws, chunked key split" if chunks else "tileattn_fwd"
+        log(f"{HEADLINE}, one of {w.Hkv} head shards (B={sh.B}, Hq={sh.Hq}, Hkv=1; {entry}): "
+            f"median {med*1e3:.1f} us min {mn*1e3:.1f} us -> {sh.flop()/med/1e9:.1f} TFLOP/s "
+            f"({sh.flop()/med/1e9/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
 
 
 def visible_pairs(mask, Hq, Sq, Sk, causal, block=64):
@@ -338,7 +359,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["matmul", "rowwise"],
+    ap.add_argument("--only", choices=["matmul", "rowwise", "shard"],
                     help="time only those kernels (stderr) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (calibrates the HBM byte counters)")
@@ -372,6 +393,9 @@ def main():
     if args.only == "rowwise":
         rowwise_lines(ta, args.steps, args.warmup)
         return
+    if args.only == "shard":
+        shard_lines(ta, args.steps, args.warmup, plain=False)
+        return
 
     if args.all:
         matmul_lines(ta, args.steps, args.warmup)
@@ -404,18 +428,7 @@ def main():
             log(f"{HEADLINE} + {what}: median {t*1e6:.1f} us -> {flop/t/1e12:.1f} TFLOP/s "
                 f"on visible pairs ({flop/t/1e12/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
 
-        # One GPU's share of the headline if its KV heads were spread over
-        # Hkv GPUs (head sharding needs no communication): the same call on
-        # one KV head and its query heads.
-        from dataclasses import replace
-
-        sh = replace(w, name=f"{HEADLINE} head shard", Hq=w.Hq // w.Hkv, Hkv=1)
-        for chunks in (False, True):
-            _, _, med, mn = time_workload(ta, sh, args.steps, args.warmup, key_chunks=chunks)
-            entry = "tileattn_fwd_ws, chunked key split" if chunks else "tileattn_fwd"
-            log(f"{HEADLINE}, one of {w.Hkv} head shards (B={sh.B}, Hq={sh.Hq}, Hkv=1; {entry}): "
-                f"median {med*1e3:.1f} us min {mn*1e3:.1f} us -> {sh.flop()/med/1e9:.1f} TFLOP/s "
-                f"({sh.flop()/med/1e9/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
+        shard_lines(ta, args.steps, args.warmup, plain=True)
 
     w = WORKLOADS[HEADLINE]
     wall, mean, med, mn = time_workload(ta, w, args.steps, args.warmup)
