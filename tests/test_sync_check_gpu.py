@@ -6,7 +6,8 @@ phases of every tile iteration.  That changes only the order in which the
 waves reach LDS, never the arithmetic, so its outputs must equal the product
 library's bit for bit.  Any difference would mean that some LDS read races the
 write it depends on, which a tolerance check against the oracle could miss.
-Both libraries are called through their C ABI (``tileattn_fwd_ext``) on the
+Both libraries are called through their C ABI (``tileattn_fwd_ext``, and
+``tileattn_fwd_ws`` for the chunked key split and its merge kernel) on the
 same device buffers.
 """
 
@@ -85,6 +86,43 @@ def test_barrier_build_is_bit_identical(libs, case):
         assert rc == 0, ta.tileattn_strerror(rc)
         outs.append((o, lse))
     torch.cuda.synchronize()
+    (o1, l1), (o2, l2) = outs
+    assert torch.equal(o1, o2), "O differs between the product and the barrier build"
+    assert torch.equal(l1, l2), "lse differs between the product and the barrier build"
+
+
+CHUNK_CASES = [
+    # B, Hq, Hkv, Sq, Sk, D, causal, fp16: shapes the chunked key split takes
+    (1, 4, 1, 4000, 4000, 128, True, False),
+    (1, 32, 8, 3, 9000, 64, False, True),
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES)
+def test_chunked_barrier_build_is_bit_identical(libs, case):
+    # The chunked key split (tileattn_fwd_ws: partial states through global
+    # memory, then the merge kernel) in both builds.
+    B, Hq, Hkv, Sq, Sk, D, causal, f16 = case
+    need = ta.tileattn_fwd_workspace_size(B, Hq, Hkv, Sq, Sk, D, causal)
+    assert need > 0
+    _say(f"sync check, chunked: B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} D={D} causal={causal} fp16={f16}")
+    q, k, v = (t.cuda() for t in random_qkv(B, Hq, Hkv, Sq, Sk, D, dtype="fp16" if f16 else "bf16",
+                                           seed=Sq + Sk))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    outs = []
+    for lib in (ta.load_library(), ctypes.CDLL(SYNC_CHECK_OUT)):
+        fn = lib.tileattn_fwd_ws
+        fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
+        fn.restype = i
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
+        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                B, Hq, Hkv, Sq, Sk, D, 1.0 / D ** 0.5, int(causal), int(f16), ws.data_ptr(), need,
+                torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, ta.tileattn_strerror(rc)
+        torch.cuda.synchronize()
+        outs.append((o, lse))
     (o1, l1), (o2, l2) = outs
     assert torch.equal(o1, o2), "O differs between the product and the barrier build"
     assert torch.equal(l1, l2), "lse differs between the product and the barrier build"
