@@ -166,3 +166,40 @@ def test_decode_rows_against_32k_keys():
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention(q, k, v, scale, False)
     _check(o, lse, o_ref, lse_ref, "bf16", "all rows")
+
+
+def _draw(case):
+    # Seeded shapes that the chunked key split takes: short queries against
+    # 3K-40K keys (non-causal), or causal heads of 3K-4.5K positions (one or
+    # two heads, to keep the oracle within a few seconds).
+    rng = np.random.default_rng(5000 + case)
+    D = int(rng.choice([64, 128]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    dtype = str(rng.choice(["bf16", "fp16"]))
+    if case % 2:
+        B, Hkv = 1, 1
+        Hq = int(rng.choice([1, 2]))
+        G = Hq
+        Sq = Sk = int(rng.integers(3100, 4500))
+        causal = True
+    else:
+        B, Hkv = int(rng.integers(1, 3)), int(rng.choice([1, 2]))
+        Hq = Hkv * G
+        Sq = int(rng.integers(1, 300))
+        Sk = int(rng.integers(3100, 40000))
+        causal = False  # top-left causal rows this short would see < 300 keys
+    return B, Hq, Hkv, Sq, Sk, D, causal, dtype
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_chunked_random_case(case):
+    B, Hq, Hkv, Sq, Sk, D, causal, dtype = _draw(case)
+    what = f"case {case}: B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} D={D} causal={causal} {dtype}"
+    _say(what)
+    assert ta.tileattn_fwd_workspace_size(B, Hq, Hkv, Sq, Sk, D, causal) > 0, "no chunks for this case"
+    q, k, v = random_qkv(B, Hq, Hkv, Sq, Sk, D, dtype=dtype, seed=6000 + case)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    o, lse = ta.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal)
+    _check(o, lse, o_ref, lse_ref, dtype, what)
