@@ -15,9 +15,11 @@
 // Troubleshooting note on fp16 accumulators).
 //
 // CDNA4 mapping (our design, not the pages'):
-//   * One workgroup = 8 waves = 256 query rows of one (batch, query head);
-//     each wave owns 32 query rows for the whole key loop.  Two waves share
-//     each SIMD (wave w and w+4).
+//   * One workgroup = 8 waves = 256 query rows: P query heads that share one
+//     KV head (P the largest power of two dividing the group size, at most
+//     8) times 256 / P consecutive positions; each wave owns 32 query rows
+//     (one head, 32 positions) for the whole key loop.  Two waves share each
+//     SIMD (wave w and w+4).
 //   * The kernel computes the transposed products S^T = K * Q^T and
 //     O^T = V^T * P^T with v_mfma_f32_32x32x16_bf16.  In the 32x32 result
 //     layout a lane holds 16 entries of ONE output column, so with queries as
@@ -49,7 +51,8 @@
 //     masking code runs only on tiles that cross a wave's diagonal or the
 //     ragged end.  A wave whose rows end before the workgroup's last tile
 //     runs the remaining tiles fully masked (p = 0), which keeps both wave
-//     groups in step with the shared barriers.
+//     groups in step with the shared barriers; with heads packed, a
+//     workgroup spans fewer positions and so fewer such tiles (none at 64).
 //   * Workgroup ids are remapped so the workgroups that one XCD (8 per chip,
 //     ids dealt round-robin) runs share key/value heads and read their K/V
 //     tiles from that XCD's L2, and each XCD takes its causal query tiles
@@ -59,7 +62,10 @@
 //     hold, each group running the same ping-pong over its own half of the
 //     key tiles (its own LDS slots); at the end the two partial
 //     (acc, l, max) states of a row merge through LDS by the online-softmax
-//     update itself.
+//     update itself.  Where a few query tiles own long key ranges, the
+//     workspace entry point also cuts those ranges into chunks run by
+//     separate workgroups, whose partial states a second kernel merges
+//     (attn_merge_kernel).
 //   * Instances with a block mask compact the visible key tiles into an LDS
 //     list and skip, per wave, the tiles its rows cannot see; instances with
 //     a linear (ALiBi) bias start the score product from the bias, and walk
