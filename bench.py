@@ -77,7 +77,7 @@ def time_workload(ta, w, steps, warmup, key_chunks=False):
     if key_chunks:
         n = ta.tileattn_fwd_workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, w.causal)
         ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
-        step = raw_launcher(ta, ta.tileattn_fwd_ws, *ptrs, int(q.dtype == torch.float16), ws.data_ptr(), n,
+        step = raw_launcher(ta, ta.tileattn_fwd_ws, *ptrs, None, int(q.dtype == torch.float16), ws.data_ptr(), n,
                             stream.cuda_stream)
     else:
         step = raw_launcher(ta, fn, *ptrs, stream.cuda_stream)

@@ -151,6 +151,11 @@ int tileattn_fwd_ext(const void* q, const void* k, const void* v, void* o, float
  * heads, causal heads whose diagonal query tiles dominate, short queries
  * against a long context): there the plain grid leaves most compute units
  * idle while its heaviest query tiles run.
+ *   alibi_slopes    : NULL, or the linear bias of tileattn_fwd_ext (Hq fp32
+ *                     slopes on the device, 4-byte aligned; same reading
+ *                     and limits): the call is then tileattn_fwd_ext
+ *                     without a block mask, up to the rounding order of the
+ *                     fold.
  *   workspace       : device memory, 16-byte aligned, of at least
  *                     tileattn_fwd_workspace_size(...) bytes for the same
  *                     problem on the same device; owned by the caller, its
@@ -159,15 +164,15 @@ int tileattn_fwd_ext(const void* q, const void* k, const void* v, void* o, float
  *                     ordered (one stream, or synchronised).
  *   workspace_bytes : its size in bytes.
  * Where tileattn_fwd_workspace_size is 0 the call is tileattn_fwd /
- * tileattn_fwd_f16 and workspace may be NULL.  Otherwise it launches two
- * kernels on `stream`.  Extra error: TILEATTN_ERR_WORKSPACE (workspace NULL
- * or workspace_bytes too small), TILEATTN_ERR_ALIGNMENT for a misaligned
- * workspace.
+ * tileattn_fwd_f16 (with slopes: tileattn_fwd_ext) and workspace may be
+ * NULL.  Otherwise it launches two kernels on `stream`.  Extra errors:
+ * TILEATTN_ERR_WORKSPACE (workspace NULL or workspace_bytes too small),
+ * TILEATTN_ERR_ALIGNMENT for a misaligned workspace or alibi_slopes.
  */
 int tileattn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int Hq, int Hkv, int Sq, int Sk, int D,
-                    float scale, int causal, int is_f16, void* workspace,
-                    size_t workspace_bytes, void* stream);
+                    float scale, int causal, const float* alibi_slopes, int is_f16,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes tileattn_fwd_ws needs for this problem on the current
@@ -194,7 +199,8 @@ long long tileattn_fwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, in
  */
 int tileattn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
                          int B, int Hq, int Hkv, int Sq, int Sk, int D,
-                         float scale, int causal, int is_f16, void* stream);
+                         float scale, int causal, const float* alibi_slopes, int is_f16,
+                         void* stream);
 
 /*
  * float32 attention forward: the same contract as tileattn_fwd with fp32

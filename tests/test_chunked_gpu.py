@@ -27,7 +27,7 @@ import torch
 
 import oracle
 import tiled_attention_tileattn_amd as ta
-from tiled_attention_tileattn_amd.inputs import WORKLOADS, make_inputs, random_qkv
+from tiled_attention_tileattn_amd.inputs import WORKLOADS, alibi_slopes, make_inputs, random_qkv
 
 pytestmark = pytest.mark.gpu
 
@@ -109,7 +109,7 @@ def test_chunked_is_deterministic_and_reusable():
         o = torch.empty_like(x[0])
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
         rc = ta.tileattn_fwd_ws(x[0].data_ptr(), x[1].data_ptr(), x[2].data_ptr(), o.data_ptr(),
-                                lse.data_ptr(), B, Hq, Hkv, Sq, Sk, D, scale, causal, 0,
+                                lse.data_ptr(), B, Hq, Hkv, Sq, Sk, D, scale, causal, None, 0,
                                 ws.data_ptr(), ws.numel(), stream)
         assert rc == 0, ta.tileattn_strerror(rc)
         return o, lse
@@ -203,3 +203,33 @@ def test_chunked_random_case(case):
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention(q, k, v, scale, causal)
     _check(o, lse, o_ref, lse_ref, dtype, what)
+
+
+ALIBI_CASES = [
+    # B, Hq, Hkv, Sq, Sk, D, causal, dtype, slopes ("geo": the ALiBi recipe)
+    (1, 4, 1, 4000, 4000, 128, True, "bf16", "geo"),     # causal: walks its chunk from the diagonal down
+    (1, 8, 2, 1, 20000, 128, False, "bf16", "geo"),      # decode rows, |i - j| bias
+    (2, 2, 2, 150, 7000, 64, False, "fp16", "geo"),
+    (1, 2, 1, 3300, 3300, 64, True, "fp16", [0.5, 0.0]),  # a steep slope and none
+]
+
+
+@pytest.mark.parametrize("case", ALIBI_CASES)
+def test_chunked_alibi(case):
+    # The linear bias through tileattn_fwd_ws: every chunk starts its scores
+    # from the bias of its own key tiles.  Against the biased oracle, and
+    # against tileattn_fwd_ext (no chunks).
+    B, Hq, Hkv, Sq, Sk, D, causal, dtype, sl = case
+    what = f"ALiBi B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} D={D} causal={causal} {dtype}"
+    _say(what)
+    assert ta.tileattn_fwd_workspace_size(B, Hq, Hkv, Sq, Sk, D, causal) > 0
+    q, k, v = random_qkv(B, Hq, Hkv, Sq, Sk, D, dtype=dtype, seed=Sq + Sk)
+    slopes = alibi_slopes(Hq) if sl == "geo" else torch.tensor(sl, dtype=torch.float32)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    qd, kd, vd, sd = q.cuda(), k.cuda(), v.cuda(), slopes.cuda()
+    o, lse = ta.forward(qd, kd, vd, causal=causal, scale=scale, alibi_slopes=sd)
+    o1, lse1 = ta.forward(qd, kd, vd, causal=causal, scale=scale, alibi_slopes=sd, key_chunks=False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ext(q, k, v, scale, causal, slopes, None)
+    _check(o, lse, o_ref, lse_ref, dtype, "chunked")
+    _check(o1, lse1, o_ref, lse_ref, dtype, "unsplit")

@@ -113,12 +113,12 @@ def test_chunked_barrier_build_is_bit_identical(libs, case):
     outs = []
     for lib in (ta.load_library(), ctypes.CDLL(SYNC_CHECK_OUT)):
         fn = lib.tileattn_fwd_ws
-        fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
+        fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, vp, ctypes.c_size_t, vp]
         fn.restype = i
         o = torch.empty_like(q)
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
         rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                B, Hq, Hkv, Sq, Sk, D, 1.0 / D ** 0.5, int(causal), int(f16), ws.data_ptr(), need,
+                B, Hq, Hkv, Sq, Sk, D, 1.0 / D ** 0.5, int(causal), None, int(f16), ws.data_ptr(), need,
                 torch.cuda.current_stream().cuda_stream)
         assert rc == 0, ta.tileattn_strerror(rc)
         torch.cuda.synchronize()

@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import tiled_attention_tileattn_amd as ta
-from tiled_attention_tileattn_amd.inputs import random_qkv
+from tiled_attention_tileattn_amd.inputs import alibi_slopes, random_qkv
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,7 @@ def _device():
     torch.cuda.synchronize()
 
 
-def _both(B, Hq, Hkv, Sq, Sk, D, causal, dtype, seed):
+def _both(B, Hq, Hkv, Sq, Sk, D, causal, dtype, seed, slopes=None):
     _say(f"no-alloc vs workspace entry: B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} D={D} "
          f"causal={causal} {dtype}")
     q, k, v = (t.cuda() for t in random_qkv(B, Hq, Hkv, Sq, Sk, D, dtype=dtype, seed=seed))
@@ -49,7 +49,7 @@ def _both(B, Hq, Hkv, Sq, Sk, D, causal, dtype, seed):
         o = torch.full_like(q, float("nan"))
         lse = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device="cuda")
         args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                B, Hq, Hkv, Sq, Sk, D, scale, causal, is_f16)
+                B, Hq, Hkv, Sq, Sk, D, scale, causal, None if slopes is None else slopes.data_ptr(), is_f16)
         if static:
             rc = ta.tileattn_fwd_noalloc(*args, stream)
         else:
@@ -72,6 +72,10 @@ def test_noalloc_matches_workspace_entry_two_calls_in_a_row():
         ta.tileattn_fwd_workspace_size(1, 2, 1, 200, 3390, 128, False) > 0
     _both(1, 4, 1, 8192, 8192, 128, True, "bf16", seed=3)
     _both(1, 2, 1, 200, 3390, 128, False, "bf16", seed=4)
+
+
+def test_noalloc_with_linear_bias():
+    _both(1, 8, 2, 2, 12000, 64, False, "bf16", seed=7, slopes=alibi_slopes(8).cuda())
 
 
 def test_noalloc_fp16_decode_and_unsplit_problem():

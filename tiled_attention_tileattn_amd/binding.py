@@ -65,11 +65,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tileattn_fwd_f16.restype = i
     lib.tileattn_fwd_ext.argtypes = sig[:13] + [vp, vp, i, i, vp]
     lib.tileattn_fwd_ext.restype = i
-    lib.tileattn_fwd_ws.argtypes = sig[:13] + [i, vp, ctypes.c_size_t, vp]
+    lib.tileattn_fwd_ws.argtypes = sig[:13] + [vp, i, vp, ctypes.c_size_t, vp]
     lib.tileattn_fwd_ws.restype = i
     lib.tileattn_fwd_workspace_size.argtypes = [i] * 7
     lib.tileattn_fwd_workspace_size.restype = ctypes.c_longlong
-    lib.tileattn_fwd_noalloc.argtypes = sig[:13] + [i, vp]
+    lib.tileattn_fwd_noalloc.argtypes = sig[:13] + [vp, i, vp]
     lib.tileattn_fwd_noalloc.restype = i
     lib.tileattn_fwd_f32.argtypes = sig
     lib.tileattn_fwd_f32.restype = i
@@ -107,10 +107,10 @@ def tileattn_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, alib
                                            int(bool(is_f16)), stream)
 
 
-def tileattn_fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, is_f16, workspace,
-                    workspace_bytes, stream) -> int:
+def tileattn_fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, alibi_slopes, is_f16,
+                    workspace, workspace_bytes, stream) -> int:
     return load_library().tileattn_fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, float(scale),
-                                          int(bool(causal)), int(bool(is_f16)), workspace,
+                                          int(bool(causal)), alibi_slopes, int(bool(is_f16)), workspace,
                                           workspace_bytes, stream)
 
 
@@ -118,9 +118,10 @@ def tileattn_fwd_workspace_size(B, Hq, Hkv, Sq, Sk, D, causal) -> int:
     return load_library().tileattn_fwd_workspace_size(B, Hq, Hkv, Sq, Sk, D, int(bool(causal)))
 
 
-def tileattn_fwd_noalloc(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, is_f16, stream) -> int:
+def tileattn_fwd_noalloc(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, alibi_slopes, is_f16,
+                         stream) -> int:
     return load_library().tileattn_fwd_noalloc(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, float(scale),
-                                               int(bool(causal)), int(bool(is_f16)), stream)
+                                               int(bool(causal)), alibi_slopes, int(bool(is_f16)), stream)
 
 
 def tileattn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream) -> int:
@@ -173,11 +174,12 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     [1 or Hq, ceil(Sq/64), ceil(Sk/64)]), both on q's device, select
     ``tileattn_fwd_ext`` (bf16 or fp16 inputs only).
 
-    Plain bf16 / fp16 calls go through ``tileattn_fwd_ws`` when
-    ``key_chunks`` is true (the default): where the library splits query
-    tiles' key ranges over several workgroups, its workspace is a torch
-    allocation on the launch stream.  ``key_chunks=False`` calls
-    ``tileattn_fwd`` / ``tileattn_fwd_f16``, which never split.
+    bf16 / fp16 calls without a block mask go through ``tileattn_fwd_ws``
+    when ``key_chunks`` is true (the default): where the library splits
+    query tiles' key ranges over several workgroups, its workspace is a
+    torch allocation on the launch stream.  ``key_chunks=False`` calls
+    ``tileattn_fwd`` / ``tileattn_fwd_f16`` / ``tileattn_fwd_ext``, which
+    never split.
     """
     import torch
 
@@ -234,7 +236,7 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
         ws_bytes = 0
-        if key_chunks and not ext and q.dtype != torch.float32:
+        if key_chunks and block_mask is None and q.dtype != torch.float32:
             ws_bytes = tileattn_fwd_workspace_size(B, Hq, Hkv, Sq, Sk, D, causal)
             if ws_bytes < 0:
                 raise TileAttnError(ws_bytes, "tileattn_fwd_workspace_size")
@@ -244,8 +246,9 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
             if s != torch.cuda.current_stream(q.device):
                 ws.record_stream(s)
             rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                    B, Hq, Hkv, Sq, Sk, D, scale, causal, int(q.dtype == torch.float16),
-                    ws.data_ptr(), ws_bytes, s.cuda_stream)
+                    B, Hq, Hkv, Sq, Sk, D, scale, causal,
+                    None if alibi_slopes is None else alibi_slopes.data_ptr(),
+                    int(q.dtype == torch.float16), ws.data_ptr(), ws_bytes, s.cuda_stream)
         elif ext:
             rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                     B, Hq, Hkv, Sq, Sk, D, scale, causal,

@@ -1130,17 +1130,17 @@ ChunkPlan chunk_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, bool causal)
   return plan;
 }
 
-template <int D, bool IS_F16>
+template <int D, bool IS_F16, bool ALIBI>
 int launch_chunked(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
-                   int B, int Hq, int Hkv, int Sq, int Sk, float scale, int causal,
+                   int B, int Hq, int Hkv, int Sq, int Sk, float scale, int causal, const float* slopes,
                    const ChunkPlan& plan, float* ws, void* stream) {
   using T = Bf16Tile<D, true>;
   const int st = causal
-      ? launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, true, IS_F16, false, false, true>, q, k, v, o,
-                                          lse, B, Hq, Hkv, Sq, Sk, scale, nullptr, nullptr, 1, plan.pack_shift,
+      ? launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, true, IS_F16, false, ALIBI, true>, q, k, v, o,
+                                          lse, B, Hq, Hkv, Sq, Sk, scale, slopes, nullptr, 1, plan.pack_shift,
                                           stream, plan.chunk_tiles, plan.max_chunks, ws)
-      : launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, false, IS_F16, false, false, true>, q, k, v, o,
-                                          lse, B, Hq, Hkv, Sq, Sk, scale, nullptr, nullptr, 1, plan.pack_shift,
+      : launch16<T::kBlockM, T::kThreads>(attn_fwd_16_kernel<D, false, IS_F16, false, ALIBI, true>, q, k, v, o,
+                                          lse, B, Hq, Hkv, Sq, Sk, scale, slopes, nullptr, 1, plan.pack_shift,
                                           stream, plan.chunk_tiles, plan.max_chunks, ws);
   if (st != TILEATTN_OK) return st;
   int pack_shift = plan.pack_shift;
@@ -1209,29 +1209,34 @@ int fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int 
 #undef TILEATTN_V16
 }
 
-// tileattn_fwd_ws: the chunked key split where chunk_plan takes it (plain
-// bf16 / fp16 only), else the plain kernel.
+// tileattn_fwd_ws: the chunked key split where chunk_plan takes it (bf16 /
+// fp16, with or without the linear bias), else the unsplit kernel.
 int fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-           int Hkv, int Sq, int Sk, int D, float scale, int causal, int is_f16, void* workspace,
-           size_t workspace_bytes, void* stream) {
+           int Hkv, int Sq, int Sk, int D, float scale, int causal, const float* slopes, int is_f16,
+           void* workspace, size_t workspace_bytes, void* stream) {
   bool empty;
   const int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty);
   if (st != TILEATTN_OK || empty) return st;
+  if (slopes != nullptr && (reinterpret_cast<uintptr_t>(slopes) & 3u) != 0) return TILEATTN_ERR_ALIGNMENT;
   const ChunkPlan plan = chunk_plan(B, Hq, Hkv, Sq, Sk, D, causal != 0);
   if (plan.chunk_tiles == 0)
-    return is_f16 ? fwd16<true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, nullptr, nullptr, 1, stream)
-                  : fwd16<false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, nullptr, nullptr, 1, stream);
+    return is_f16 ? fwd16<true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, slopes, nullptr, 1, stream)
+                  : fwd16<false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, slopes, nullptr, 1, stream);
   if (workspace == nullptr || workspace_bytes < plan.bytes) return TILEATTN_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return TILEATTN_ERR_ALIGNMENT;
   auto qq = static_cast<const uint16_t*>(q), kk = static_cast<const uint16_t*>(k),
        vv = static_cast<const uint16_t*>(v);
   auto oo = static_cast<uint16_t*>(o);
   auto ws = static_cast<float*>(workspace);
-  if (D == 128)
-    return is_f16 ? launch_chunked<128, true>(qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, causal, plan, ws, stream)
-                  : launch_chunked<128, false>(qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, causal, plan, ws, stream);
-  return is_f16 ? launch_chunked<64, true>(qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, causal, plan, ws, stream)
-                : launch_chunked<64, false>(qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, causal, plan, ws, stream);
+#define TILEATTN_CHUNKED(DD, FF, AA) \
+  launch_chunked<DD, FF, AA>(qq, kk, vv, oo, lse, B, Hq, Hkv, Sq, Sk, scale, causal, slopes, plan, ws, stream)
+  if (slopes != nullptr) {
+    if (D == 128) return is_f16 ? TILEATTN_CHUNKED(128, true, true) : TILEATTN_CHUNKED(128, false, true);
+    return is_f16 ? TILEATTN_CHUNKED(64, true, true) : TILEATTN_CHUNKED(64, false, true);
+  }
+  if (D == 128) return is_f16 ? TILEATTN_CHUNKED(128, true, false) : TILEATTN_CHUNKED(128, false, false);
+  return is_f16 ? TILEATTN_CHUNKED(64, true, false) : TILEATTN_CHUNKED(64, false, false);
+#undef TILEATTN_CHUNKED
 }
 
 }  // namespace
@@ -1303,25 +1308,28 @@ extern "C" long long tileattn_fwd_workspace_size(int B, int Hq, int Hkv, int Sq,
 
 extern "C" int tileattn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
-                               int causal, int is_f16, void* workspace, size_t workspace_bytes,
-                               void* stream) {
-  return fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, is_f16, workspace,
+                               int causal, const float* alibi_slopes, int is_f16, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, alibi_slopes, is_f16, workspace,
                 workspace_bytes, stream);
 }
 
 extern "C" int tileattn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
                                     int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
-                                    int causal, int is_f16, void* stream) {
+                                    int causal, const float* alibi_slopes, int is_f16, void* stream) {
   bool empty;
   const int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty);
   if (st != TILEATTN_OK || empty) return st;
+  if (alibi_slopes != nullptr && (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u) != 0) return TILEATTN_ERR_ALIGNMENT;
   const ChunkPlan plan = chunk_plan(B, Hq, Hkv, Sq, Sk, D, causal != 0);
-  if (plan.chunk_tiles == 0)  // no chunks: the plain kernel, no workspace
-    return fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, is_f16, nullptr, 0, stream);
+  if (plan.chunk_tiles == 0)  // no chunks: the unsplit kernel, no workspace
+    return fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, alibi_slopes, is_f16, nullptr, 0,
+                  stream);
   if (plan.bytes > kScratchBytes) return TILEATTN_ERR_SCRATCH;
   float* const ws = scratch_address();
   if (ws == nullptr) return TILEATTN_ERR_LAUNCH;
-  return fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, is_f16, ws, kScratchBytes, stream);
+  return fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, alibi_slopes, is_f16, ws, kScratchBytes,
+                stream);
 }
 
 extern "C" int tileattn_fwd_f32(const float* q, const float* k, const float* v, float* o,
