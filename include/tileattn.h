@@ -32,9 +32,12 @@
  *     q   [B, Hq,  Sq, D]      k, v [B, Hkv, Sk, D]
  *     o   [B, Hq,  Sq, D]      lse  [B, Hq,  Sq]      (fp32)
  * All pointers are device pointers on the current HIP device, 16-byte
- * aligned.  The caller owns every buffer; the library allocates nothing,
- * keeps no state between calls and is safe to call from several host
- * threads.  o and lse must not overlap q, k or v.
+ * aligned.  The caller owns every buffer, and no call allocates memory.
+ * Between calls the library keeps only per-device constants (the compute
+ * unit count; for tileattn_fwd_noalloc, the address of its static device
+ * workspace), and it is safe to call from several host threads (calls that
+ * share a workspace must still be ordered).  o and lse must not overlap q,
+ * k or v.
  *
  * Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  * stream).  Argument errors are reported before anything is launched; a
