@@ -233,3 +233,20 @@ def test_chunked_alibi(case):
     o_ref, lse_ref = oracle.attention_ext(q, k, v, scale, causal, slopes, None)
     _check(o, lse, o_ref, lse_ref, dtype, "chunked")
     _check(o1, lse1, o_ref, lse_ref, dtype, "unsplit")
+
+
+def test_chunked_on_a_side_stream():
+    # forward() on a stream other than the current one: the workspace it
+    # allocates is recorded on that stream, so back-to-back calls there (each
+    # freeing its workspace to the allocator on return) still give the same
+    # result as one call on the current stream.
+    B, Hq, Hkv, Sq, Sk, D = 1, 8, 2, 64, 12000, 128
+    assert ta.tileattn_fwd_workspace_size(B, Hq, Hkv, Sq, Sk, D, False) > 0
+    q, k, v = (t.cuda() for t in random_qkv(B, Hq, Hkv, Sq, Sk, D, dtype="bf16", seed=77))
+    o_ref, l_ref = ta.forward(q, k, v)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    outs = [ta.forward(q, k, v, stream=side) for _ in range(4)]
+    side.synchronize()
+    for o, lse in outs:
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
