@@ -319,7 +319,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
       if (lane == 0) tcount = count;
     }
     __syncthreads();
-    nt = tcount;
+    nt = __builtin_amdgcn_readfirstlane(tcount);  // wave-uniform, so branches on it stay scalar
   }
   // With a causal linear bias the largest scores of a row sit next to its
   // diagonal: walking the tiles from the diagonal down finds the row max on
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
     v_voff = row_in * kRowBytes + ((p ^ vswz(row_in)) << 4);
   }
-  auto dma_tile = [&](const __amdgpu_buffer_rsrc_t& rsrc, bool is_k, int t, int slot) {
+  auto dma_tile = [&](__amdgpu_buffer_rsrc_t rsrc, bool is_k, int t, int slot) {
     const int tile_off = t * kBlockN * kRowBytes;
 #pragma unroll
     for (int e = 0; e < kDmaPieces; ++e) {
@@ -456,13 +456,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   // rest immediates.
   const int s16 = lane & 15;
   unsigned kofs[D / 16], vofs[D / 32];
+  // The offsets include this group's slot pair, so that within a tile
+  // iteration only the slot parity (a compile-time immediate) is added.
 #pragma unroll
-  for (int a = 0; a < D / 16; ++a) kofs[a] = l32 * kRowBytes + (((2 * a + half) ^ kswz(l32)) << 4);
+  for (int a = 0; a < D / 16; ++a)
+    kofs[a] = kslot(0) + l32 * kRowBytes + (((2 * a + half) ^ kswz(l32)) << 4);
   {
     const int vr = 4 * half + (s16 >> 2);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
-      vofs[db] = vr * kRowBytes + 64 * (db ^ (vswz(vr) >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (s16 & 3);
+      vofs[db] = vslot(0) + vr * kRowBytes + 64 * (db ^ (vswz(vr) >> 2)) + 32 * ((lane >> 4) & 1) +
+                 8 * (s16 & 3);
   }
   auto k_operand = [&](int kbase, int i) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(smem + kbase + kofs[i >> 1] + (i & 1) * 32 * kRowBytes);
@@ -496,10 +500,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
 
   // Matrix phase: S_j (WITH_S) and acc += V_{j-1}^T P_{j-1}^T (WITH_PV),
   // MFMA by MFMA alternating, operands read kP steps ahead.
-  auto matrix_body = [&](auto with_s_c, auto with_pv_c, int j) {
+  auto matrix_body = [&](auto with_s_c, auto with_pv_c, int j, auto par) {
     constexpr bool WITH_S = decltype(with_s_c)::value;
     constexpr bool WITH_PV = decltype(with_pv_c)::value;
-    const int kb = kslot(j), vb = vslot(j - 1);
+    // Tile j's K and tile j-1's V sit in the slots of parity j & 1 and
+    // (j - 1) & 1: byte offsets from the pair's first slots (compile-time
+    // constants inside the loop, where par is an integral_constant).
+    const int kb = static_cast<int>(par) * T::kKBytes;
+    const int vb = (1 - static_cast<int>(par)) * T::kVBytes;
+    // Keep the operand offsets opaque here, so that the compiler folds
+    // kb + ... into each read's immediate instead of hoisting every
+    // offset + constant out of the loop into a register of its own (not in
+    // the bias instances, which take runtime parities; see the tile loop).
+    if constexpr (!ALIBI) {
+#pragma unroll
+      for (int a = 0; a < D / 16; ++a) asm volatile("" : "+v"(kofs[a]));
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) asm volatile("" : "+v"(vofs[d]));
+    }
     if (TILEATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
     bf16x8 kring[kP], vring[kP];
 #pragma unroll
@@ -525,18 +543,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   };
   // With a block mask, a wave skips the products of the tiles its query
   // block cannot see: their probabilities would all be 0.
-  auto matrix_phase = [&](auto with_s_c, auto with_pv_c, int j) {
+  auto matrix_phase = [&](auto with_s_c, auto with_pv_c, int j, auto par) {
     using TT_ = std::true_type;
     using FF_ = std::false_type;
     constexpr bool WITH_S = decltype(with_s_c)::value;
     constexpr bool WITH_PV = decltype(with_pv_c)::value;
     if constexpr (!MASK) {
-      matrix_body(with_s_c, with_pv_c, j);
+      matrix_body(with_s_c, with_pv_c, j, par);
     } else {
       // Two independent products, one after the other, each behind its own
       // wave-uniform branch (one body with both would need four variants).
-      if (WITH_S && wave_sees(j)) matrix_body(TT_{}, FF_{}, j);
-      if (WITH_PV && wave_sees(j - 1)) matrix_body(FF_{}, TT_{}, j);
+      if (WITH_S && wave_sees(j)) matrix_body(TT_{}, FF_{}, j, par);
+      if (WITH_PV && wave_sees(j - 1)) matrix_body(FF_{}, TT_{}, j, par);
     }
   };
 
@@ -626,16 +644,41 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     // wave writes V_0 there.
     if constexpr (T::kStageOverV) __syncthreads();
 
+    // Tiles in pairs (odd j, then even j), so that each matrix phase has its
+    // slot parity as a compile-time constant and the slot offsets fold into
+    // the LDS instructions' immediates (the compiler does not unroll a loop
+    // with barriers by itself).  The bias instances, at the register limit,
+    // keep one tile per loop step and a runtime parity.
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    constexpr bool kPairs = !ALIBI;
+    int j = 1;
     if (group == 0) {
-      iteration(0, [&] { matrix_phase(TT{}, FF{}, 0); }, [&] { vector_phase(0); });
-      for (int j = 1; j < nt; ++j)
-        iteration(j, [&] { matrix_phase(TT{}, TT{}, j); }, [&] { vector_phase(j); });
-      iteration(nt, [&] { matrix_phase(FF{}, TT{}, nt); }, [&] {});
+      iteration(0, [&] { matrix_phase(TT{}, FF{}, 0, P0{}); }, [&] { vector_phase(0); });
+      if constexpr (kPairs) {
+        for (; j + 1 < nt; j += 2) {
+          iteration(j, [&] { matrix_phase(TT{}, TT{}, j, P1{}); }, [&] { vector_phase(j); });
+          iteration(j + 1, [&] { matrix_phase(TT{}, TT{}, j + 1, P0{}); }, [&] { vector_phase(j + 1); });
+        }
+        if (j < nt) iteration(j, [&] { matrix_phase(TT{}, TT{}, j, P1{}); }, [&] { vector_phase(j); });
+      } else {
+        for (; j < nt; ++j)
+          iteration(j, [&] { matrix_phase(TT{}, TT{}, j, j & 1); }, [&] { vector_phase(j); });
+      }
+      iteration(nt, [&] { matrix_phase(FF{}, TT{}, nt, nt & 1); }, [&] {});
     } else {
-      iteration(0, [&] {}, [&] { matrix_phase(TT{}, FF{}, 0); });
-      for (int j = 1; j < nt; ++j)
-        iteration(j, [&] { vector_phase(j - 1); }, [&] { matrix_phase(TT{}, TT{}, j); });
-      iteration(nt, [&] { vector_phase(nt - 1); }, [&] { matrix_phase(FF{}, TT{}, nt); });
+      iteration(0, [&] {}, [&] { matrix_phase(TT{}, FF{}, 0, P0{}); });
+      if constexpr (kPairs) {
+        for (; j + 1 < nt; j += 2) {
+          iteration(j, [&] { vector_phase(j - 1); }, [&] { matrix_phase(TT{}, TT{}, j, P1{}); });
+          iteration(j + 1, [&] { vector_phase(j); }, [&] { matrix_phase(TT{}, TT{}, j + 1, P0{}); });
+        }
+        if (j < nt) iteration(j, [&] { vector_phase(j - 1); }, [&] { matrix_phase(TT{}, TT{}, j, P1{}); });
+      } else {
+        for (; j < nt; ++j)
+          iteration(j, [&] { vector_phase(j - 1); }, [&] { matrix_phase(TT{}, TT{}, j, j & 1); });
+      }
+      iteration(nt, [&] { vector_phase(nt - 1); }, [&] { matrix_phase(FF{}, TT{}, nt, nt & 1); });
     }
   }
 
