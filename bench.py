@@ -8,10 +8,16 @@ grouped-query workload B=1, Hq=32, Hkv=8, Sq=Sk=8192, D=128, bf16, with
 inputs already resident in HBM.  Prints ONE JSON line on stdout; extra
 diagnostics go to stderr.
 
+The default warmup (100 launches, about 45 ms) outlasts the GPU's power
+management transient: after an idle spell the first ~40 launches of this
+workload run up to 25% slower than the sustained rate while the engine
+clock settles, so the timed steps measure the sustained rate.
+
 FLOP per step = 4*B*Hq*Sq*Sk*D, halved for causal.  The roofline object
 prices the kernel against MI355X's dense bf16 MFMA peak (2.5 PFLOP/s:
 256 CUs x 2048 bf16 FMA/clk x 2 x 2.4 GHz = 2516.6 TFLOP/s), with the
-kernel's duration taken from HIP events recorded on the launch stream.
+kernel's mean launch duration taken from one pair of HIP events around the
+timed launches on the launch stream (span / steps).
 The CPU baseline is the fp64 oracle run on the same workload on the host's
 cores.  ``traffic`` is the kernel's HBM bytes per launch from the committed
 rocprofv3 counter summary in profiles/ (null when the kernel changed since).
@@ -83,19 +89,33 @@ def time_workload(ta, w, steps, warmup, key_chunks=False):
         step = raw_launcher(ta, fn, *ptrs, stream.cuda_stream)
     for _ in range(warmup):
         step()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
+    # Per-launch events for the median and minimum: a pass of its own after
+    # the warmup, so that the timed launches are the last ones of the run.
+    n = min(steps, 50)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
         starts[i].record(stream)
         step()
         ends[i].record(stream)
+    # The timed region: K launches back to back between one pair of events on
+    # the launch stream, so the mean launch duration is the events' span / K
+    # (the short gaps between launches included).  Events around every launch
+    # would add their own packets between the kernels (about 7 us a step).
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_start.record(stream)
+    for _ in range(steps):
+        step()
+    t_end.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    mean_ms = t_start.elapsed_time(t_end) / steps
     ev = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     del q, k, v, o, lse
-    return wall_ms, float(ev.mean()), float(np.median(ev)), float(ev.min())
+    return wall_ms, mean_ms, float(np.median(ev)), float(ev.min())
 
 
 def shard_lines(ta, steps, warmup, plain):
@@ -355,8 +375,8 @@ def profiled_traffic():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["matmul", "rowwise", "shard"],

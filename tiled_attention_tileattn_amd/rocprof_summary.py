@@ -80,6 +80,17 @@ def trace_stats(d: str, key: str):
     raise KeyError(key)
 
 
+def trace_timed(d: str, key: str, last: int):
+    """Durations (ns) of the last ``last`` dispatches of the kernel, in
+    launch order: the timed steps of a bench.py run, which follow its warmup
+    launches."""
+    rows = [r for r in _csv(d, "kernel_trace.csv") if _match(key, r["Kernel_Name"])]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows[-last:]]
+    return {"calls": len(dur), "avg_ns": statistics.fmean(dur), "median_ns": statistics.median(dur),
+            "min_ns": float(min(dur)), "max_ns": float(max(dur))}
+
+
 def _match(key: str, name: str) -> bool:
     return all(part in name for part in key.split("&"))
 
@@ -105,13 +116,17 @@ def generic(a):
     cf, cw, f_scale, w_scale = copy_scales(a.copy_fetch, a.copy_write)
     lines = [f"# rocprofv3: {a.title}", "",
              "Kernel trace (with --stats) and FETCH_SIZE / WRITE_SIZE passes, each a separate run.",
+             (f"Times are means over each kernel's last {a.timed} dispatches (the timed steps)."
+              if a.timed else "Times are means over every dispatch."),
              f"Counter bytes are scaled by what the counters read for a plain 256 MiB copy "
              f"(FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}).", "",
              "| kernel | workload | calls | avg time | algorithmic rate | HBM fetch | HBM write | algorithmic bytes |",
              "|---|---|---|---|---|---|---|---|"]
     figs = []
     for k in spec:
-        tr = trace_stats(a.trace, k["key"])
+        # With --timed N, the mean over each kernel's last N dispatches (the
+        # timed steps after bench.py's warmup); else over all of them.
+        tr = trace_timed(a.trace, k["key"], a.timed) if a.timed else trace_stats(a.trace, k["key"])
         fk = counters_matching(a.fetch, k["key"]).get("FETCH_SIZE", float("nan"))
         wk = counters_matching(a.write, k["key"]).get("WRITE_SIZE", float("nan"))
         fb, wb = fk * 1024.0 * f_scale, wk * 1024.0 * w_scale
@@ -149,6 +164,8 @@ def main():
     ap.add_argument("--flop", type=float, default=549755813888.0)
     ap.add_argument("--compulsory-bytes", type=float, default=168820736.0)
     ap.add_argument("--commands", nargs="*", default=[])
+    ap.add_argument("--timed", type=int, default=None,
+                    help="generic form: average each kernel over its last N dispatches")
     ap.add_argument("--bench-log", default=None,
                     help="stdout of the profiled bench.py run (its JSON line)")
     a = ap.parse_args()
@@ -170,12 +187,17 @@ def main():
     w_scale = COPY_BYTES / (cw * 1024.0)
     fetch_b = fetch_kib * 1024.0 * f_scale
     write_b = write_kib * 1024.0 * w_scale
-    avg_s = tr["avg_ns"] * 1e-9
     bench = None
     if a.bench_log:
         for line in open(a.bench_log):
             if line.startswith("{"):
                 bench = json.loads(line)
+    # The kernel time the figures use: the mean over bench.py's timed steps
+    # (the last ``steps`` dispatches), as bench.py's own events measure it;
+    # without the bench line, over every dispatch.
+    timed = trace_timed(a.trace, KERNEL_KEY, bench["steps"]) if bench else None
+    avg_ns = timed["avg_ns"] if timed else tr["avg_ns"]
+    avg_s = avg_ns * 1e-9
     gui = sq.get("GRBM_GUI_ACTIVE", float("nan"))
     xcds = 8
     simds = 1024
@@ -188,8 +210,11 @@ def main():
         "kernel": KERNEL_KEY,
         "workload": a.workload,
         "source_sha256_16": source_hash(),
-        "avg_kernel_ns": tr["avg_ns"],
+        "avg_kernel_ns": avg_ns,
+        "timed_dispatches": timed["calls"] if timed else None,
+        "median_kernel_ns": timed["median_ns"] if timed else None,
         "calls": tr["calls"],
+        "all_dispatches_avg_ns": tr["avg_ns"],
         "tflops_at_avg": a.flop / avg_s / 1e12,
         "fetch_bytes": fetch_b,
         "write_bytes": write_b,
@@ -215,7 +240,11 @@ def main():
         "| figure | value |",
         "|---|---|",
         f"| dispatches profiled | {tr['calls']} |",
-        f"| average kernel time | {tr['avg_ns']/1e3:.1f} us (min {tr['min_ns']/1e3:.1f}, max {tr['max_ns']/1e3:.1f}) |",
+        (f"| average kernel time, bench.py's {timed['calls']} timed steps (the last dispatches) | "
+         f"{avg_ns/1e3:.1f} us (median {timed['median_ns']/1e3:.1f}, min {timed['min_ns']/1e3:.1f}, "
+         f"max {timed['max_ns']/1e3:.1f}) |") if timed else "| timed steps | not identified (no bench line) |",
+        f"| average kernel time, all dispatches (warmup included) | {tr['avg_ns']/1e3:.1f} us "
+        f"(min {tr['min_ns']/1e3:.1f}, max {tr['max_ns']/1e3:.1f}) |",
         f"| TFLOP/s at the average (counted FLOP {a.flop:.4g}) | {fig['tflops_at_avg']:.1f} |",
         (f"| bench.py's own HIP-event mean in the traced run | {fig['bench_event_mean_ns']/1e3:.1f} us "
          f"(roofline.achieved {bench['roofline']['achieved']:.1f} TFLOP/s) |") if bench else "| bench.py line | not recorded |",
