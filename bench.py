@@ -61,6 +61,39 @@ def raw_launcher(ta, fn, *args):
     return step
 
 
+def time_steps(step, steps, warmup, stream=None):
+    """Time a launch function: ``warmup`` untimed calls, a pass of min(steps,
+    50) calls with events around each one (for the median and minimum), then
+    the timed region: ``steps`` calls back to back between one pair of
+    events on the launch stream.  Returns (wall ms per call by the host
+    clock, mean ms per call by the events' span, median ms, minimum ms).
+    Events around every launch add their own packets between the kernels
+    (about 7 us a step), so the mean, not the median, prices a launch."""
+    stream = stream or torch.cuda.current_stream()
+    for _ in range(warmup):
+        step()
+    n = min(steps, 50)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_start.record(stream)
+    for _ in range(steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    mean_ms = t_start.elapsed_time(t_end) / steps
+    ev = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    return wall_ms, mean_ms, float(np.median(ev)), float(ev.min())
+
+
 def time_workload(ta, w, steps, warmup, key_chunks=False):
     """Return (ms_per_step wall, mean kernel ms from events, median, min).
 
@@ -87,35 +120,9 @@ def time_workload(ta, w, steps, warmup, key_chunks=False):
                             stream.cuda_stream)
     else:
         step = raw_launcher(ta, fn, *ptrs, stream.cuda_stream)
-    for _ in range(warmup):
-        step()
-    # Per-launch events for the median and minimum: a pass of its own after
-    # the warmup, so that the timed launches are the last ones of the run.
-    n = min(steps, 50)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    for i in range(n):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    # The timed region: K launches back to back between one pair of events on
-    # the launch stream, so the mean launch duration is the events' span / K
-    # (the short gaps between launches included).  Events around every launch
-    # would add their own packets between the kernels (about 7 us a step).
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    t_start.record(stream)
-    for _ in range(steps):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    mean_ms = t_start.elapsed_time(t_end) / steps
-    ev = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    times = time_steps(step, steps, warmup, stream)
     del q, k, v, o, lse
-    return wall_ms, mean_ms, float(np.median(ev)), float(ev.min())
+    return times
 
 
 def shard_lines(ta, steps, warmup, plain):
@@ -130,11 +137,11 @@ def shard_lines(ta, steps, warmup, plain):
     w = WORKLOADS[HEADLINE]
     sh = replace(w, name=f"{HEADLINE} head shard", Hq=w.Hq // w.Hkv, Hkv=1)
     for chunks in ((False, True) if plain else (True,)):
-        _, _, med, mn = time_workload(ta, sh, steps, warmup, key_chunks=chunks)
+        _, mean, med, mn = time_workload(ta, sh, steps, warmup, key_chunks=chunks)
         entry = "tileattn_fwd_ws, chunked key split" if chunks else "tileattn_fwd"
         log(f"{HEADLINE}, one of {w.Hkv} head shards (B={sh.B}, Hq={sh.Hq}, Hkv=1; {entry}): "
-            f"median {med*1e3:.1f} us min {mn*1e3:.1f} us -> {sh.flop()/med/1e9:.1f} TFLOP/s "
-            f"({sh.flop()/med/1e9/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
+            f"mean {mean*1e3:.1f} us (median {med*1e3:.1f}, min {mn*1e3:.1f}) -> {sh.flop()/mean/1e9:.1f} TFLOP/s "
+            f"({sh.flop()/mean/1e9/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
 
 
 def visible_pairs(mask, Hq, Sq, Sk, causal, block=64):
@@ -184,33 +191,16 @@ def time_ext(ta, w, steps, warmup, mask, alibi=True):
                        None if slopes is None else slopes.data_ptr(),
                        None if mask is None else mask.data_ptr(), 1 if mask is None else mask.shape[0],
                        int(q.dtype == torch.float16), stream.cuda_stream)
-    for _ in range(warmup):
-        run()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    for a, b in ev:
-        a.record(stream)
-        run()
-        b.record(stream)
-    torch.cuda.synchronize()
-    t = np.median([a.elapsed_time(b) for a, b in ev]) * 1e-3
+    _, mean_ms, _, _ = time_steps(run, steps, warmup, stream)
+    t = mean_ms * 1e-3
     return t, 4.0 * w.B * w.D * pairs
 
 
 def time_events(fn, steps, warmup):
-    """Median and mean of ``steps`` launches of fn, HIP events on the current stream."""
-    stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        fn()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    for a, b in ev:
-        a.record(stream)
-        fn()
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in ev]
-    return float(np.median(ms)) * 1e-3, float(np.mean(ms)) * 1e-3
+    """(mean, median) seconds per call of fn on the current stream: the mean
+    over the timed region, the median over a per-launch pass (time_steps)."""
+    _, mean_ms, med_ms, _ = time_steps(fn, steps, warmup)
+    return mean_ms * 1e-3, med_ms * 1e-3
 
 
 def matmul_lines(ta, steps, warmup):
@@ -223,13 +213,13 @@ def matmul_lines(ta, steps, warmup):
         flop = 2.0 * M * N * K
         for dt, dname in ((torch.float32, "fp32"), (torch.bfloat16, "bf16")):
             c = torch.empty((M, N), dtype=dt, device="cuda")
-            med, mean = time_events(lambda: ta.matmul(a, b, out=c), steps, warmup)
-            log(f"{name} (M=N=K={M}, C {dname}): median {med*1e6:.1f} us mean {mean*1e6:.1f} us "
-                f"-> {flop/med/1e12:.1f} TFLOP/s ({flop/med/1e12/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
+            mean, med = time_events(lambda: ta.matmul(a, b, out=c), steps, warmup)
+            log(f"{name} (M=N=K={M}, C {dname}): mean {mean*1e6:.1f} us median {med*1e6:.1f} us "
+                f"-> {flop/mean/1e12:.1f} TFLOP/s ({flop/mean/1e12/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
         c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-        med, _ = time_events(lambda: torch.matmul(a, b, out=c), steps, warmup)
-        log(f"{name}: torch.matmul (ROCm library GEMM, C bf16, context only): median {med*1e6:.1f} us "
-            f"-> {flop/med/1e12:.1f} TFLOP/s")
+        mean, _ = time_events(lambda: torch.matmul(a, b, out=c), steps, warmup)
+        log(f"{name}: torch.matmul (ROCm library GEMM, C bf16, context only): mean {mean*1e6:.1f} us "
+            f"-> {flop/mean/1e12:.1f} TFLOP/s")
         del a, b, c
 
 
@@ -267,27 +257,27 @@ def rowwise_lines(ta, steps, warmup):
             x = random_rows(*shape, seed=seed, dtype=dtype, device="cuda")
             out = torch.empty_like(x)
             nbytes = 2.0 * x.numel() * esize
-            med, mean = time_events(lambda: ta.softmax(x, out=out), steps, warmup)
+            mean, med = time_events(lambda: ta.softmax(x, out=out), steps, warmup)
             bufs = (x, out)
         else:
             x, w, b = random_gelu_inputs(shape[0], seed=seed, dtype=dtype, device="cuda")
             out = torch.empty_like(x)
             nbytes = 4.0 * x.numel() * esize
-            med, mean = time_events(lambda: ta.gelu(x, w, b, out=out), steps, warmup)
+            mean, med = time_events(lambda: ta.gelu(x, w, b, out=out), steps, warmup)
             bufs = (x, w, b, out)
-        log(f"{name}: median {med*1e6:.1f} us mean {mean*1e6:.1f} us -> {nbytes/med/1e9:.0f} GB/s "
-            f"({nbytes/med/1e9/PEAK_HBM_GBS*100:.1f}% of HBM peak; {nbytes/2**30:.2f} GiB per launch)")
+        log(f"{name}: mean {mean*1e6:.1f} us median {med*1e6:.1f} us -> {nbytes/mean/1e9:.0f} GB/s "
+            f"({nbytes/mean/1e9/PEAK_HBM_GBS*100:.1f}% of HBM peak; {nbytes/2**30:.2f} GiB per launch)")
         if kind == "softmax":
-            med, _ = time_events(lambda: torch.softmax(x, dim=1, out=out), steps, warmup)
-            log(f"{name}: torch.softmax (context only): median {med*1e6:.1f} us -> {nbytes/med/1e9:.0f} GB/s")
+            mean, _ = time_events(lambda: torch.softmax(x, dim=1, out=out), steps, warmup)
+            log(f"{name}: torch.softmax (context only): mean {mean*1e6:.1f} us -> {nbytes/mean/1e9:.0f} GB/s")
         del bufs, x, out
     # What a plain streaming copy reaches on this device (context for the rates above).
     src = torch.empty(1 << 29, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
-    med, _ = time_events(lambda: dst.copy_(src), steps, warmup)
+    mean, _ = time_events(lambda: dst.copy_(src), steps, warmup)
     nbytes = 2.0 * src.numel() * 4
-    log(f"device copy 2 GiB -> 2 GiB (torch copy_, context only): median {med*1e6:.1f} us -> "
-        f"{nbytes/med/1e9:.0f} GB/s ({nbytes/med/1e9/PEAK_HBM_GBS*100:.1f}% of HBM peak)")
+    log(f"device copy 2 GiB -> 2 GiB (torch copy_, context only): mean {mean*1e6:.1f} us -> "
+        f"{nbytes/mean/1e9:.0f} GB/s ({nbytes/mean/1e9/PEAK_HBM_GBS*100:.1f}% of HBM peak)")
     del src, dst
 
 
@@ -426,8 +416,8 @@ def main():
             st = 3 if name == "longctx_gqa_bf16" else args.steps
             wu = 2 if name == "longctx_gqa_bf16" else args.warmup
             wall, mean, med, mn = time_workload(ta, w, st, wu)
-            log(f"{name}: median {med*1e3:.1f} us min {mn*1e3:.1f} us "
-                f"-> {w.flop()/med/1e9:.1f} TFLOP/s ({w.flop()/med/1e9/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
+            log(f"{name}: mean {mean*1e3:.1f} us (median {med*1e3:.1f}, min {mn*1e3:.1f}) "
+                f"-> {w.flop()/mean/1e9:.1f} TFLOP/s ({w.flop()/mean/1e9/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
             if not args.no_cpu:
                 cb = cpu_baseline(w, sample_rows=256 if name == "longctx_gqa_bf16" else None)
                 log(f"{name}: CPU oracle {cb['value']:.3g} TFLOP/s on {cb['cores']} cores ({cb['sample']})")
@@ -445,7 +435,7 @@ def main():
                  ("ALiBi + 1024-key local window + sink block", win, True)]
         for what, mask, alibi in cases:
             t, flop = time_ext(ta, w, args.steps, args.warmup, mask, alibi)
-            log(f"{HEADLINE} + {what}: median {t*1e6:.1f} us -> {flop/t/1e12:.1f} TFLOP/s "
+            log(f"{HEADLINE} + {what}: mean {t*1e6:.1f} us -> {flop/t/1e12:.1f} TFLOP/s "
                 f"on visible pairs ({flop/t/1e12/PEAK_BF16_TFLOPS*100:.1f}% of bf16 peak)")
 
         shard_lines(ta, args.steps, args.warmup, plain=True)
