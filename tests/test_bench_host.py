@@ -84,3 +84,66 @@ def test_cpu_baseline_repeats_passes_and_names_them():
     assert cb["sample"].startswith(f"the whole workload ({w.B * w.Hq * w.Sq} query rows), ")
     assert " pass" in cb["sample"] and "fp64 numpy oracle" in cb["sample"]
     assert cb["sample"].endswith(f" on {bench.cpu_model()}")
+
+
+class _FakeEvent:
+    """Stands in for torch.cuda.Event: records where in the call sequence it
+    was recorded, and reports elapsed time as the number of steps between."""
+
+    def __init__(self, log):
+        self.log = log
+        self.pos = None
+
+    def record(self, stream=None):
+        self.pos = len(self.log)
+        self.log.append("event")
+
+    def elapsed_time(self, other):
+        return float(sum(1 for x in self.log[self.pos:other.pos] if x == "step"))
+
+
+def test_time_steps_times_the_last_launches(monkeypatch):
+    """The timed region is the last ``steps`` launches of the run, after the
+    warmup and the per-launch pass, between one pair of events (the profile
+    summary averages the last ``steps`` dispatches on that basis)."""
+    log = []
+    monkeypatch.setattr(bench.torch.cuda, "Event", lambda enable_timing=True: _FakeEvent(log))
+    monkeypatch.setattr(bench.torch.cuda, "synchronize", lambda: None)
+    steps, warmup = 7, 5
+    wall, mean, med, mn = bench.time_steps(lambda: log.append("step"), steps, warmup, stream=object())
+    calls = [x for x in log if x == "step"]
+    assert len(calls) == warmup + min(steps, 50) + steps
+    # the per-launch pass: an event on each side of each launch
+    per = warmup + 3 * min(steps, 50)
+    assert log[:warmup] == ["step"] * warmup
+    assert log[warmup:per] == ["event", "step", "event"] * min(steps, 50)
+    # the timed region: one event, exactly `steps` launches, one event, nothing after
+    assert log[per:] == ["event"] + ["step"] * steps + ["event"]
+    assert mean == 1.0 and med == 1.0 and mn == 1.0  # fake ms per launch
+    assert wall >= 0.0
+
+
+def test_profile_summary_averages_the_last_dispatches(tmp_path):
+    """rocprof_summary.trace_timed takes the last N dispatches of the kernel by
+    start time, whatever order the trace rows come in, and ignores others."""
+    from tiled_attention_tileattn_amd import rocprof_summary as rs
+
+    rows = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
+    t = 0
+    durs = []
+    for i in range(12):
+        d = 1000 + 100 * i  # ns; later dispatches take longer
+        rows.append(f'"attn_fwd_16_kernel<128, true, false, false, false, false>(args)",{t},{t + d}')
+        rows.append(f'"other_kernel",{t + d},{t + d + 5}')
+        durs.append(d)
+        t += d + 10
+    # shuffle the data rows: selection must go by timestamp
+    body = rows[1:]
+    body = body[1::2] + body[0::2][::-1]
+    d = tmp_path / "trace"
+    d.mkdir()
+    (d / "run_kernel_trace.csv").write_text("\n".join([rows[0]] + body) + "\n")
+    got = rs.trace_timed(str(d), rs.KERNEL_KEY, 5)
+    assert got["calls"] == 5
+    assert got["avg_ns"] == sum(durs[-5:]) / 5
+    assert got["min_ns"] == durs[-5] and got["max_ns"] == durs[-1]
